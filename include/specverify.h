@@ -1,0 +1,227 @@
+/*
+ * specverify.h - C ABI of the speculative-decoding verification pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call of the pass scores the current token plus K drafted positions of
+ * one sequence (M = K + 1 rows, 1 <= M <= 16) in a single stream over
+ * GGUF-quantised weights, with int8 activations and integer dot products
+ * ("Inside OpenJet Engine: making speculative decoding pay", sections "The
+ * bottleneck: reading weights for a small amount of work" and "One GPU
+ * launch for a speculative cycle"; "How Kinetic is fast", section "RAD-1:
+ * exact speculative decoding").  It ends in a full-vocabulary head whose
+ * logits feed greedy or rejection-sampling acceptance.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless a comment says host.  The caller
+ *    owns every buffer; no call allocates or frees memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls are asynchronous on it and return only validation / launch
+ *    status.  Outputs are ready when the stream has reached the call.
+ *  - Arguments are validated before anything is launched; on a non-zero
+ *    status nothing was enqueued and sv_last_error() holds a message.
+ *  - Layouts are row-major; "[M][K]" means M rows of K contiguous values.
+ *  - Results are deterministic, and every output row depends only on its
+ *    own input row: a row of an M-row call is bit-identical to the same row
+ *    run alone (batch invariance, "How Kinetic is fast", section "Why the
+ *    output does not change").
+ *  - The library is stateless and thread-safe.  Calls on different streams
+ *    may run concurrently if their output buffers do not overlap.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (return value of every int-returning call). */
+#define SV_OK 0
+#define SV_ERR_ARG (-1)       /* NULL where not allowed, bad mode, M out of range */
+#define SV_ERR_SHAPE (-2)     /* a dimension is not a multiple of the block size */
+#define SV_ERR_ALIGN (-3)     /* a pointer is not aligned as documented */
+#define SV_ERR_QTYPE (-4)     /* unsupported quantisation type */
+#define SV_ERR_WORKSPACE (-5) /* workspace too small */
+#define SV_ERR_HIP (-6)       /* the HIP runtime reported an error */
+
+/* GGUF tensor type ids of the supported weight formats (the formats ggml
+ * defines, "How Kinetic is fast", section "References"). */
+#define SV_Q8_0 8  /* 32-element blocks: fp16 d, 32 x int8;          8.5 bits/weight */
+#define SV_Q4_K 12 /* 256-element super-blocks: fp16 d, dmin, 6-bit sub-scales and
+                      mins per 32, 4-bit quants;                    4.5 bits/weight */
+#define SV_Q6_K 14 /* 256-element super-blocks: 6-bit quants, int8 scale per 16,
+                      fp16 d;                                       6.5625 bits/weight */
+
+#define SV_MAX_M 16
+
+/* Human-readable text of the last non-OK status on the calling thread. */
+const char *sv_last_error(void);
+
+/* Library version string (host memory, static). */
+const char *sv_version(void);
+
+/* ------------------------------------------------------------------ */
+/* a1. Load-time weight repack.                                        */
+/* ------------------------------------------------------------------ */
+/* Bytes of the repacked form of a rows x cols matrix of type qtype, or 0
+ * for an unsupported type or shape (cols must be a multiple of 32 for Q8_0
+ * and of 256 for Q4_K / Q6_K).  The repacked form holds exactly the bytes of
+ * the GGUF form (same size), rearranged. */
+size_t sv_repacked_bytes(int32_t qtype, int64_t rows, int64_t cols);
+
+/* Rearranges canonical GGUF blocks into the aligned stream layout the
+ * projection kernels read, changing no value ("Inside OpenJet Engine",
+ * section "One GPU launch for a speculative cycle": Q6_K and Q8_0 weights are
+ * rearranged at load time for aligned access without changing their values).
+ *   gguf_src: rows x (cols / block) GGUF blocks, contiguous, any alignment.
+ *   dst:      sv_repacked_bytes(...) bytes, 256-byte aligned.
+ * Layout of dst (all streams row-major, one record per row per block):
+ *   Q8_0: int8 quants [rows][cols] | fp16 d [rows][cols/32]
+ *   Q4_K: 16-byte quant records [rows][cols/32] (byte i holds elements i and
+ *         i+16 of the 32-element sub-block in its low and high nibble) |
+ *         the 16-byte super-block headers (d, dmin, packed scales) verbatim
+ *         [rows][cols/256]
+ *   Q6_K: 16-byte low-nibble records [rows][cols/32] (as Q4_K) | 8-byte
+ *         high-bit records [rows][cols/32] (dword h, byte i, bits 2t..2t+1 =
+ *         high bits of element 16h + 4t + i) | int8 scales [rows][cols/16] |
+ *         fp16 d [rows][cols/256]
+ * src and dst must not overlap. */
+int sv_repack_weights(int32_t qtype, const void *gguf_src, void *dst, int64_t rows, int64_t cols,
+                      void *stream);
+
+/* Inverse of sv_repack_weights (for verification of the load path). */
+int sv_unpack_weights(int32_t qtype, const void *repacked, void *gguf_dst, int64_t rows,
+                      int64_t cols, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* a2. Activation quantiser Q8A32.                                     */
+/* ------------------------------------------------------------------ */
+/* Per row m and 32-element block b of v = x (times gamma when given, one
+ * fp32 rounding per element): amax = max |v|, d = amax / 127 (fp32),
+ * id = d ? 1/d : 0, q = clamp(roundf(v * id), -127, 127) (round half away
+ * from zero), and the exact int sums of q over each 16-element half
+ * ("Inside OpenJet Engine", "One GPU launch...": int8 activations).
+ *   x [M][K] fp32, gamma [K] fp32 or NULL, K % 32 == 0, 1 <= M <= 16.
+ *   q [M][K] int8, d [M][K/32] fp32, s16 [M][K/16] int32.
+ *   sumsq [M][K/32] fp32 or NULL: sum of x^2 (before gamma) of each block,
+ *   the partials an RMS norm of x is formed from (see sv_act). */
+int sv_quantize_act_q8(const float *x, int32_t M, int64_t K, const float *gamma, int8_t *q,
+                       float *d, int32_t *s16, float *sumsq, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* a3/a4. Projection of M positions in one weight stream.              */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    int32_t qtype;    /* SV_Q8_0 / SV_Q4_K / SV_Q6_K */
+    int64_t rows;     /* output features N */
+    int64_t cols;     /* input features K */
+    const void *data; /* repacked weights (sv_repack_weights), 256-byte aligned */
+} sv_weight;
+
+/* An int8 activation as written by sv_quantize_act_q8 or by an epilogue.
+ * When sumsq_parts is given, the input is the RMS-normalised vector
+ * r * v with r[m] = 1 / sqrt(sum_i sumsq_parts[m][i] / K + eps); r is
+ * folded into every output of the consumer (y = r * W.v_q), so the int8
+ * codes never depend on it. */
+typedef struct {
+    int32_t M;                /* positions, 1..16 */
+    int64_t K;                /* features */
+    const int8_t *q;          /* [M][K] */
+    const float *d;           /* [M][K/32] */
+    const int32_t *s16;       /* [M][K/16] */
+    const float *sumsq_parts; /* [M][n_parts] or NULL (then r = 1) */
+    int32_t n_parts;
+    float eps;
+} sv_act;
+
+#define SV_EP_NONE 0  /* write y only */
+#define SV_EP_QUANT 1 /* also requantise y[src] * gamma for the next consumer */
+#define SV_EP_PAIR 2  /* also requantise (y[0] * y[1]) * gamma (gate x up) */
+
+/* Fused producer epilogue ("Inside OpenJet Engine", "One GPU launch...": the
+ * producing phase requantises activations for the next consumer, including
+ * the next RMS normalisation's weight).  Output rows must be a multiple of 32.
+ * The new activation has K' = rows; its sumsq partials are the per-block sums
+ * of the (unnormalised) vector that was quantised, [M][rows/32]. */
+typedef struct {
+    int32_t mode;       /* SV_EP_* */
+    int32_t src;        /* SV_EP_QUANT: which output is requantised */
+    const float *gamma; /* [rows] or NULL (= all ones) */
+    int8_t *q;          /* [M][rows] */
+    float *d;           /* [M][rows/32] */
+    int32_t *s16;       /* [M][rows/16] */
+    float *sumsq;       /* [M][rows/32] */
+} sv_epilogue;
+
+/* Y_j[m][n] = r[m] * sum over 32-blocks b of the exact int32 block sum of
+ * weight quants times activation quants, scaled by the block's weight and
+ * activation scales (fp32), for each of n_w matrices W[0..n_w-1] that share
+ * the input A (q, k, v, or gate, up).  All W[j] have the same rows and
+ * cols = A->K.  y[j] is [M][rows] fp32 or NULL.  ep may be NULL.
+ * The fp32 combine order depends only on cols (never on M), which makes
+ * every row batch-invariant. */
+int sv_verify_matvec(const sv_weight *W, int32_t n_w, const sv_act *A, float *const *y,
+                     const sv_epilogue *ep, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* a6/a9. Output head with fused argmax.                               */
+/* ------------------------------------------------------------------ */
+/* logits[m][i] = projection of row row_ids[i] of H (all rows when row_ids is
+ * NULL, then n_rows = H->rows) for input A; the same arithmetic as
+ * sv_verify_matvec, so a row's logit does not depend on which other rows are
+ * scored ("Inside OpenJet Engine", "Cheap drafting, careful state
+ * management": a restricted draft head over a token subset plus tokens added
+ * dynamically, while verification keeps the full vocabulary).
+ *   logits [M][n_rows] fp32 or NULL; argmax [M] uint64 or NULL:
+ *   argmax[m] = (orderable bits of the max logit) << 32 | (0xFFFFFFFF - i)
+ *   for the winning index i (ties go to the lowest i); the token is
+ *   row_ids[i] (or i).  sv_argmax_token decodes it on the host. */
+int sv_head_logits(const sv_weight *H, const sv_act *A, const int32_t *row_ids, int64_t n_rows,
+                   float *logits, uint64_t *argmax, void *stream);
+
+/* Host helper: index encoded in a packed argmax word. */
+int64_t sv_argmax_index(uint64_t packed);
+
+/* ------------------------------------------------------------------ */
+/* a7. Greedy acceptance.                                              */
+/* ------------------------------------------------------------------ */
+/* Row i's top token judges draft i: n = number of leading drafts equal to
+ * the top token of their row; the round emits drafts[0..n-1] and then the
+ * top token of row n ("How Kinetic is fast", "Why the output does not
+ * change": greedy keeps a guess only when it is the model's top token).
+ *   argmax [K+1] packed words from sv_head_logits; row_ids as given to it
+ *   (or NULL); drafts [K] int32, 0 <= K <= 15.
+ *   out [K+2] int32: out[0] = n, out[1..n+1] = emitted tokens. */
+int sv_accept_greedy(const uint64_t *argmax, const int32_t *row_ids, const int32_t *drafts,
+                     int32_t K, int32_t *out, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* a8. Rejection-sampling acceptance (fp64).                           */
+/* ------------------------------------------------------------------ */
+/* p_i = softmax(logits_i / temperature) in fp64.
+ * General drafter (q != NULL, [K][V] fp32 draft distributions): accept x_i
+ * iff u[i][0] * q_i(x_i) < p_i(x_i) (u < min(1, p/q)); on the first rejection
+ * emit the smallest j with cumsum_j(max(0, p_i - q_i)) > u[i][1] * R_i (R_i =
+ * the residual's total; p_i itself if R_i == 0) and stop; if all K are
+ * accepted emit one token from p_K with u[K][1] ("Speculative Decoding with
+ * Open-Weights Models", section "Mathematical Integrity: Rejection Sampling
+ * for LLMs", the alpha and p' equations).
+ * Certain one-token drafter (q == NULL): for i = 0..K, t_i = smallest j with
+ * cumsum_j(p_i) > u[i][0]; accept while i < K and t_i == x_i, else emit t_i
+ * and stop; this uses one uniform per emitted token in order, so the tokens
+ * equal plain sampling with the same uniforms ("How Kinetic is fast", "Why
+ * the output does not change").
+ *   logits [K+1][V] fp32, drafts [K] int32 (0 <= K <= 15), u [K+1][2] fp64
+ *   in [0, 1), temperature > 0, workspace of sv_accept_workspace_bytes(V, K)
+ *   bytes (8-byte aligned), out [K+2] int32 as for sv_accept_greedy. */
+size_t sv_accept_workspace_bytes(int64_t V, int32_t K);
+int sv_accept_rejection(const float *logits, int64_t V, const float *q, const int32_t *drafts,
+                        int32_t K, const double *u, float temperature, void *workspace,
+                        size_t ws_bytes, int32_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */

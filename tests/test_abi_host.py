@@ -1,0 +1,153 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every function include/specverify.h declares, sizes are right, and invalid
+arguments are rejected with the documented status before any launch."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import speculative_decoding_verification_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sv.LIB_PATH), reason="libspecverify.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", sv.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sv_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    L = sv.lib()
+    for n in names:
+        assert hasattr(L, n)
+    assert set(sv.EXPORTS) == set(names)
+
+
+def test_version():
+    assert "gfx950" in sv.version()
+
+
+@pytest.mark.parametrize("qt,rows,cols,expect", [
+    (8, 1024, 1024, 1024 * 1024 // 32 * 34),
+    (12, 2560, 2560, 2560 * 2560 // 256 * 144),
+    (14, 151936, 5120, 151936 * 5120 // 256 * 210),
+    (14, 5120, 17408, 5120 * 17408 // 256 * 210),
+    (8, 3, 48, 0),      # cols not a multiple of 32
+    (12, 4, 128, 0),    # cols not a multiple of 256
+    (3, 4, 256, 0),     # unsupported type
+    (8, 0, 32, 0),
+])
+def test_repacked_bytes(qt, rows, cols, expect):
+    assert sv.repacked_bytes(qt, rows, cols) == expect
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _err(rc, code):
+    assert rc == code, (rc, sv.lib().sv_last_error())
+    assert sv.lib().sv_last_error()
+
+
+def test_quantize_rejects():
+    L = sv.lib()
+    _err(L.sv_quantize_act_q8(FAKE, 0, 64, None, FAKE, FAKE, FAKE, None, None), sv.SV_ERR_ARG)
+    _err(L.sv_quantize_act_q8(FAKE, 17, 64, None, FAKE, FAKE, FAKE, None, None), sv.SV_ERR_ARG)
+    _err(L.sv_quantize_act_q8(FAKE, 2, 48, None, FAKE, FAKE, FAKE, None, None), sv.SV_ERR_SHAPE)
+    _err(L.sv_quantize_act_q8(None, 2, 64, None, FAKE, FAKE, FAKE, None, None), sv.SV_ERR_ARG)
+    _err(L.sv_quantize_act_q8(ctypes.c_void_p((1 << 20) + 2), 2, 64, None, FAKE, FAKE, FAKE, None, None),
+         sv.SV_ERR_ALIGN)
+
+
+def test_repack_rejects():
+    L = sv.lib()
+    _err(L.sv_repack_weights(5, FAKE, FAKE, 4, 256, None), sv.SV_ERR_QTYPE)
+    _err(L.sv_repack_weights(12, FAKE, FAKE, 4, 128, None), sv.SV_ERR_SHAPE)
+    _err(L.sv_repack_weights(12, FAKE, FAKE_ODD, 4, 256, None), sv.SV_ERR_ALIGN)
+    _err(L.sv_repack_weights(12, None, FAKE, 4, 256, None), sv.SV_ERR_ARG)
+    # overlapping source and destination
+    _err(L.sv_repack_weights(8, ctypes.c_void_p((1 << 20) + 256), FAKE, 4, 256, None), sv.SV_ERR_ARG)
+
+
+def _act(M=5, K=256, q=FAKE):
+    return sv.Act(M, K, q.value, FAKE.value, FAKE.value, None, 0, 1e-6)
+
+
+def _w(qt=12, rows=64, cols=256, data=FAKE):
+    return sv.Weight(qt, rows, cols, data.value)
+
+
+def _mv(ws, A, ep=None):
+    n = len(ws)
+    W = (sv.Weight * n)(*ws)
+    Y = (ctypes.c_void_p * n)(*([FAKE.value] * n))
+    return sv.lib().sv_verify_matvec(W, n, ctypes.byref(A), Y, None if ep is None else ctypes.byref(ep), None)
+
+
+def test_matvec_rejects():
+    _err(_mv([_w()], _act(M=0)), sv.SV_ERR_ARG)
+    _err(_mv([_w()], _act(M=17)), sv.SV_ERR_ARG)
+    _err(_mv([_w(qt=2)], _act()), sv.SV_ERR_QTYPE)
+    _err(_mv([_w(cols=512)], _act()), sv.SV_ERR_SHAPE)          # cols != K
+    _err(_mv([_w(cols=32)], _act(K=32)), sv.SV_ERR_SHAPE)       # Q4_K needs 256
+    _err(_mv([_w(data=FAKE_ODD)], _act()), sv.SV_ERR_ALIGN)
+    _err(_mv([_w()], _act(q=FAKE_ODD)), sv.SV_ERR_ALIGN)
+    _err(_mv([_w(), _w(rows=32)], _act()), sv.SV_ERR_SHAPE)     # rows differ
+    _err(_mv([_w(), _w(qt=14)], _act()), sv.SV_ERR_SHAPE)       # qtypes differ
+    W = (sv.Weight * 4)(*([_w()] * 4))
+    rc = sv.lib().sv_verify_matvec(W, 4, ctypes.byref(_act()), None, None, None)
+    _err(rc, sv.SV_ERR_ARG)
+    ep = sv.Epilogue(7, 0, None, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    _err(_mv([_w()], _act(), ep), sv.SV_ERR_ARG)
+    ep = sv.Epilogue(sv.SV_EP_PAIR, 0, None, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    _err(_mv([_w()], _act(), ep), sv.SV_ERR_ARG)                 # pair needs two
+    ep = sv.Epilogue(sv.SV_EP_QUANT, 0, None, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    _err(_mv([_w(rows=48)], _act(), ep), sv.SV_ERR_SHAPE)       # rows % 32
+    ep = sv.Epilogue(sv.SV_EP_QUANT, 3, None, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    _err(_mv([_w()], _act(), ep), sv.SV_ERR_ARG)                 # src out of range
+
+
+def test_head_and_accept_rejects():
+    L = sv.lib()
+    H = _w(qt=14)
+    _err(L.sv_head_logits(ctypes.byref(H), ctypes.byref(_act()), None, 0, None, None, None), sv.SV_ERR_ARG)
+    _err(L.sv_head_logits(ctypes.byref(H), ctypes.byref(_act()), FAKE, 0, FAKE, None, None), sv.SV_ERR_SHAPE)
+    _err(L.sv_accept_greedy(FAKE, None, FAKE, 16, FAKE, None), sv.SV_ERR_ARG)
+    _err(L.sv_accept_greedy(FAKE_ODD, None, FAKE, 4, FAKE, None), sv.SV_ERR_ALIGN)
+    ws = sv.accept_workspace_bytes(151936, 4)
+    assert ws > 0 and ws % 256 == 0
+    assert sv.accept_workspace_bytes(10, 16) == 0
+    _err(L.sv_accept_rejection(FAKE, 151936, None, FAKE, 4, FAKE, ctypes.c_float(0.0), FAKE, ws, FAKE, None),
+         sv.SV_ERR_ARG)
+    _err(L.sv_accept_rejection(FAKE, 151936, None, FAKE, 4, FAKE, ctypes.c_float(1.0), FAKE, ws - 8, FAKE, None),
+         sv.SV_ERR_WORKSPACE)
+    _err(L.sv_accept_rejection(FAKE, 0, None, FAKE, 4, FAKE, ctypes.c_float(1.0), FAKE, ws, FAKE, None),
+         sv.SV_ERR_SHAPE)
+
+
+def test_argmax_index_decode():
+    for idx in (0, 1, 151935, (1 << 31) - 1):
+        packed = (0xC0000000 << 32) | (0xFFFFFFFF - idx)
+        assert sv.argmax_index(packed) == idx
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    import importlib
+    mod = importlib.import_module("speculative_decoding_verification_amd")
+    monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(mod, "_lib", None)
+    with pytest.raises(ImportError):
+        mod.lib()
