@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the verification pass on one MI355X.
+
+A step is one verification pass at M positions (current token + M-1
+drafts) over the 4B-class chain: 36 layers of q/k/v/o and gate/up in Q4_K
+and down in Q6_K (hidden 2560, FFN 9728), the requantising epilogue between
+every pair of projections, a Q6_K output head over 151936 tokens with fused
+argmax, and greedy acceptance.  Weights and inputs are seeded synthetic data
+resident in HBM before timing starts.  Each pass is captured once in a HIP
+graph and replayed.
+
+Output: one JSON line.  `value` is the weight-stream rate in GB/s (the
+repacked weight bytes one pass reads / time per pass) at the headline M; the
+M sweep reports time per pass, GB/s, % of the 8 TB/s HBM peak and verified
+positions/s.  `roofline` gives the dominant kernel's rate from live
+per-launch HIP-event timing; `cpu_baseline` times the CPU oracle on the same
+pass on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "weight-stream GB/s (% HBM peak) and verified positions/s at M=1..5"
+SEED_BASE = 0x5EED0000
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_weights_fn(seed, keep=None):
+    import synth
+
+    def fn(layer, name, qtype, rows, cols):
+        if name.startswith("gamma:"):
+            return synth.rms_weight(rows, seed, layer, name)
+        raw = synth.gguf_weights(qtype, rows, cols, seed, layer, name)
+        if keep is not None:
+            keep[(layer, name)] = (qtype, raw)
+        return raw
+    return fn
+
+
+def time_sweep(stack, Ms, steps, warmup):
+    import torch
+    rows = []
+    for M in Ms:
+        g = stack.capture(M)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps * 1e3
+        ms = e0.elapsed_time(e1) / steps
+        rows.append({"M": M, "ms_per_pass": ms, "wall_ms_per_pass": wall})
+        log(f"M={M}: {ms:.4f} ms/pass (wall {wall:.4f})")
+        del g
+    return rows
+
+
+def calibrate_sleep():
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    e0.record()
+    torch.cuda._sleep(2_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2_000_000 / max(e0.elapsed_time(e1), 1e-3)   # cycles per ms
+
+
+def pass_launch_timing(stack, M, launches, cycles_per_ms):
+    """Duration of individual launches of the one-launch pass kernel, each
+    bracketed by its own HIP events on the launching stream and preceded by
+    ~60 us of queued GPU work, so host enqueue time never falls inside a
+    measured interval."""
+    import torch
+    p = stack.make_pass(M)
+    stack.run_pass(M, p)            # warm
+    torch.cuda.synchronize()
+    sleep = int(cycles_per_ms * 0.06)
+    recs = []
+    for _ in range(launches):
+        stack._quant_in(M)
+        torch.cuda._sleep(sleep)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        p.run()
+        b.record()
+        recs.append((a, b))
+    torch.cuda.synchronize()
+    assert p.status() == 0, "pass reported a failed wait"
+    return [a.elapsed_time(b) * 1e3 for a, b in recs]   # us
+
+
+def per_phase_timing(stack, M, passes, cycles_per_ms):
+    """Per-phase launches (one sv_verify_matvec call per phase), each timed
+    alone as above: the phase breakdown of the same pass."""
+    import torch
+    sleep = int(cycles_per_ms * 0.06)
+    recs = []
+    for _ in range(passes):
+        for label, f in stack.phases(M):
+            torch.cuda._sleep(sleep)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            recs.append((label, a, b))
+    torch.cuda.synchronize()
+    out = {}
+    for label, a, b in recs:
+        out.setdefault(label, []).append(a.elapsed_time(b) * 1e3)
+    return out
+
+
+def cpu_baseline(keep, shape, seed, M, budget_s):
+    import numpy as np
+
+    import oracle
+    import synth
+    H, F = shape.hidden, shape.ffn
+    layers = []
+    for li in range(shape.layers):
+        lw = {n: keep[(li, n)] for n in ("q", "k", "v", "o", "gate", "up", "down")}
+        for g, n in (("g1", H), ("g2", H), ("g3", H), ("g4", F)):
+            lw[g] = synth.rms_weight(n, seed, li, "gamma:" + g)
+        layers.append(lw)
+    head = None
+    if shape.vocab:
+        hq, hraw = keep[(-1, "head")]
+        head = (hq, hraw, synth.rms_weight(H, seed, -1, "gamma:final"))
+    x = synth.activations(16, H, seed, "x0")[:M]
+    threads = oracle.default_threads()
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.chain_pass(layers, x, H, F, head=head, threads=threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s or len(times) >= 20:
+            break
+    t = float(np.median(times))
+    return t, len(times), threads
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="chain4b", choices=["chain4b", "stack27b"])
+    ap.add_argument("--m", default="1,2,3,4,5", help="M sweep (positions per pass)")
+    ap.add_argument("--headline-m", type=int, default=5)
+    ap.add_argument("--roofline-launches", type=int, default=10)
+    ap.add_argument("--phase-breakdown", action="store_true", help="also time every phase as its own launch")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the verification pass of one sequence is not sharded)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_amd as sv
+    from speculative_decoding_verification_amd.chain import CHAIN_4B, STACK_27B, VerifyStack
+
+    shape = CHAIN_4B if args.config == "chain4b" else STACK_27B
+    cfg_index = 1 if args.config == "chain4b" else 3
+    seed = SEED_BASE + cfg_index
+    Ms = [int(m) for m in args.m.split(",")]
+    hm = args.headline_m if args.headline_m in Ms else Ms[-1]
+    torch.cuda.set_device(0)
+    sv.lib()
+    keep = {} if not args.no_cpu_baseline else None
+    t0 = time.perf_counter()
+    stack = VerifyStack(shape, make_weights_fn(seed, keep), max_M=max(Ms))
+    torch.cuda.synchronize()
+    log(f"loaded {args.config}: {shape.pass_bytes() / 1e9:.3f} GB in {time.perf_counter() - t0:.1f} s")
+    import synth
+    stack.x.copy_(torch.from_numpy(synth.activations(max(Ms), shape.hidden, seed, "x0")).cuda())
+    drafts = synth.token_ids(max(Ms) - 1 or 1, shape.vocab, seed, "drafts")
+    stack.drafts.copy_(torch.from_numpy(drafts).cuda())
+
+    pass_bytes = shape.pass_bytes()
+    sweep = time_sweep(stack, Ms, args.steps, args.warmup)
+    for r in sweep:
+        r["gbps"] = pass_bytes / (r["ms_per_pass"] * 1e-3) / 1e9
+        r["pct_hbm_peak"] = 100.0 * r["gbps"] / HBM_PEAK_GBPS
+        r["positions_per_s"] = r["M"] / (r["ms_per_pass"] * 1e-3)
+    t1 = next((r["ms_per_pass"] for r in sweep if r["M"] == 1), None)
+    for r in sweep:
+        r["t_over_t1"] = (r["ms_per_pass"] / t1) if t1 else None
+    head_row = next(r for r in sweep if r["M"] == hm)
+
+    # dominant kernel: the one-launch pass kernel, timed live per launch
+    cpm = calibrate_sleep()
+    us = pass_launch_timing(stack, hm, args.roofline_launches, cpm)
+    avg_us = float(np.mean(us))
+    achieved = pass_bytes / (avg_us * 1e-6) / 1e9
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+        "kernel": f"sv::pass_kernel<{hm}> (all projection phases and the head in one launch)",
+        "avg_launch_us": round(avg_us, 2), "p10_us": round(float(np.percentile(us, 10)), 2),
+        "p90_us": round(float(np.percentile(us, 90)), 2), "launches": len(us),
+        "alg_bytes_per_launch": pass_bytes,
+    }
+    if args.phase_breakdown:
+        per = per_phase_timing(stack, hm, 1, cpm)
+        roofline["eager_phases"] = {
+            k: {"avg_us": round(float(np.mean(v)), 2), "launches_per_pass": len(v),
+                "gbps": round(stack.phase_bytes(k) / (np.mean(v) * 1e-6) / 1e9, 1) if stack.phase_bytes(k) else None}
+            for k, v in per.items()}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t_cpu, n_cpu, threads = cpu_baseline(keep, shape, seed, hm, args.cpu_seconds)
+        cpu = {"value": round(pass_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n_cpu} full {args.config} pass(es) at M={hm} (36 layers + head), median "
+                         f"{t_cpu:.2f} s per pass, C oracle with {threads} threads",
+               "positions_per_s": round(hm / t_cpu, 4)}
+
+    res = {
+        "metric": METRIC,
+        "value": round(head_row["gbps"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head_row["ms_per_pass"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: hidden {shape.hidden}, ffn {shape.ffn}, {shape.layers} layers "
+                               f"(Q4_K q/k/o/gate/up, {'Q6_K' if shape.v_q == 14 else 'Q4_K'} v, Q6_K down), "
+                               f"Q6_K head {shape.vocab}x{shape.hidden}, greedy acceptance",
+                   "M": hm, "drafts": hm - 1, "bytes_per_pass": pass_bytes},
+        "pct_hbm_peak": round(head_row["pct_hbm_peak"], 2),
+        "positions_per_s": round(head_row["positions_per_s"], 1),
+        "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,7 +13,9 @@
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless a comment says host.  The caller
- *    owns every buffer; no call allocates or frees memory.
+ *    owns every buffer and passes any scratch space as a workspace; no call
+ *    allocates device memory (sv_pass_create allocates one small host
+ *    handle).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls are asynchronous on it and return only validation / launch
  *    status.  Outputs are ready when the stream has reached the call.
@@ -127,12 +129,12 @@ typedef struct {
  * codes never depend on it. */
 typedef struct {
     int32_t M;                /* positions, 1..16 */
-    int64_t K;                /* features */
+    int64_t K;                /* features, a multiple of 32, at most 24576 */
     const int8_t *q;          /* [M][K] */
     const float *d;           /* [M][K/32] */
     const int32_t *s16;       /* [M][K/16] */
     const float *sumsq_parts; /* [M][n_parts] or NULL (then r = 1) */
-    int32_t n_parts;
+    int32_t n_parts;          /* 1..576 when sumsq_parts is given */
     float eps;
 } sv_act;
 
@@ -158,12 +160,21 @@ typedef struct {
 /* Y_j[m][n] = r[m] * sum over 32-blocks b of the exact int32 block sum of
  * weight quants times activation quants, scaled by the block's weight and
  * activation scales (fp32), for each of n_w matrices W[0..n_w-1] that share
- * the input A (q, k, v, or gate, up).  All W[j] have the same rows and
- * cols = A->K.  y[j] is [M][rows] fp32 or NULL.  ep may be NULL.
- * The fp32 combine order depends only on cols (never on M), which makes
- * every row batch-invariant. */
+ * the input A (q, k, v, or gate, up).  All W[j] have the same qtype and rows,
+ * and cols = A->K.  y[j] is [M][rows] fp32 or NULL.  ep may be NULL.
+ * The K axis is cut into chunks whose number depends only on K; the fp32
+ * combine order (sequential per lane, butterfly over a lane group, chunks
+ * added in order) depends only on K, never on M, which makes every row
+ * batch-invariant and every run deterministic.
+ * workspace: sv_matvec_workspace_bytes(W, n_w, A) bytes, 256-byte aligned.
+ * Its first 256 KiB hold tile counters that must be zero before the first
+ * use; every call leaves them zero again (the rest holds partial sums and
+ * needs no initialisation), so one workspace of the largest size can serve
+ * calls of any shape.  May be NULL when the size is 0.  Calls sharing a
+ * workspace must not run concurrently. */
+size_t sv_matvec_workspace_bytes(const sv_weight *W, int32_t n_w, const sv_act *A);
 int sv_verify_matvec(const sv_weight *W, int32_t n_w, const sv_act *A, float *const *y,
-                     const sv_epilogue *ep, void *stream);
+                     const sv_epilogue *ep, void *workspace, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* a6/a9. Output head with fused argmax.                               */
@@ -174,15 +185,79 @@ int sv_verify_matvec(const sv_weight *W, int32_t n_w, const sv_act *A, float *co
  * scored ("Inside OpenJet Engine", "Cheap drafting, careful state
  * management": a restricted draft head over a token subset plus tokens added
  * dynamically, while verification keeps the full vocabulary).
+ *   row_ids: NULL or n_rows int32 ids in [0, H->rows) (an id outside that
+ *   range is a caller error; it is scored as row 0 and never read out of
+ *   bounds).
  *   logits [M][n_rows] fp32 or NULL; argmax [M] uint64 or NULL:
  *   argmax[m] = (orderable bits of the max logit) << 32 | (0xFFFFFFFF - i)
  *   for the winning index i (ties go to the lowest i); the token is
- *   row_ids[i] (or i).  sv_argmax_token decodes it on the host. */
+ *   row_ids[i] (or i).  sv_argmax_index decodes it on the host.
+ *   workspace as for sv_verify_matvec, sv_head_workspace_bytes(H, A, n_rows)
+ *   bytes (n_rows = 0 for all rows). */
+size_t sv_head_workspace_bytes(const sv_weight *H, const sv_act *A, int64_t n_rows);
 int sv_head_logits(const sv_weight *H, const sv_act *A, const int32_t *row_ids, int64_t n_rows,
-                   float *logits, uint64_t *argmax, void *stream);
+                   float *logits, uint64_t *argmax, void *workspace, size_t ws_bytes, void *stream);
 
 /* Host helper: index encoded in a packed argmax word. */
 int64_t sv_argmax_index(uint64_t packed);
+
+/* ------------------------------------------------------------------ */
+/* a5. A whole pass in one persistent launch.                          */
+/* ------------------------------------------------------------------ */
+/* One phase of a pass: the arguments of one sv_verify_matvec or
+ * sv_head_logits call.  Phase i reads what phase i-1 wrote (its A is phase
+ * i-1's epilogue output), so the phases form a chain ("Inside OpenJet
+ * Engine", "One GPU launch for a speculative cycle": all phases of a cycle in
+ * one launch, synchronised between phases, without host round trips). */
+typedef struct {
+    const sv_weight *W;      /* n_w matrices (read during sv_pass_create only) */
+    int32_t n_w;
+    sv_act A;
+    float *y[3];
+    sv_epilogue ep;          /* ep.mode = SV_EP_NONE for none */
+    const int32_t *row_ids;  /* head gather, or NULL */
+    int64_t n_rows;
+    uint64_t *argmax;        /* head argmax [M], or NULL */
+} sv_phase;
+
+typedef struct sv_pass sv_pass; /* opaque host handle */
+
+/* Device workspace for a pass: phase table, counters and partial sums. */
+size_t sv_pass_workspace_bytes(const sv_phase *phases, int32_t n_phases);
+
+/* Validates every phase (same M for all, and K/32 divisible by 32 either for
+ * all phases or for none; the epilogue outputs q, d, s16 and sumsq of all
+ * phases in 256-byte blocks of their own, never shared between phases, so
+ * no consumer can see a stale cached copy), writes the phase table into `workspace` (device,
+ * 256-byte aligned, sv_pass_workspace_bytes bytes; it must stay allocated and
+ * untouched while the pass exists) and returns a small host handle.  This
+ * call synchronises with the device; it is load-time work, not per cycle. */
+int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *workspace, size_t ws_bytes,
+                   sv_pass **out);
+
+/* Enqueues one pass on `stream`: a single persistent launch of as many
+ * workgroups as the GPU holds at once (at most two per compute unit) that
+ * works through the phases in order and leaves its counters reset for the
+ * next run.  Allocates nothing and records no memset, so it can be captured
+ * in a graph.  Runs of one pass must not overlap, and the pass expects the
+ * GPU to itself while it runs (its workgroups wait on each other).  Every
+ * wait between phases is bounded; if one ever expires the launch ends early
+ * and sv_pass_status reports it. */
+int sv_pass_run(const sv_pass *pass, void *stream);
+
+/* Host: status word of the last completed run (0 = ok; synchronous copy). */
+int sv_pass_status(const sv_pass *pass, uint32_t *status);
+
+/* Profiling.  enable != 0 makes later runs record, per workgroup and phase,
+ * four words: the 100 MHz real-time counter when the workgroup reached the
+ * phase, when its input became ready, when it finished its units, and how
+ * many units it ran ([grid][n_phases][4], zero rows for phases in which a
+ * workgroup had no unit).  With host != NULL the last run's record is
+ * copied there (synchronous; bytes >= grid * n_phases * 32).  *grid (may be
+ * NULL) receives the number of workgroups a run launches. */
+int sv_pass_trace(sv_pass *pass, int enable, uint64_t *host, size_t bytes, int32_t *grid);
+
+void sv_pass_destroy(sv_pass *pass);
 
 /* ------------------------------------------------------------------ */
 /* a7. Greedy acceptance.                                              */

@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: tests/, __graft_entry__.smoke() and the
 cpu_baseline leg of bench.py may import this package; the product path
 (``speculative_decoding_verification_amd``) never does, and the two share no
 code.  See the header of oracle.c for what each function computes and which
-page passage it follows.  The chain reading (``chain``) is described there.
+page passage it follows; ``chain_pass`` documents the reading of the layer
+chain.
 """
 
 from __future__ import annotations
@@ -191,3 +192,49 @@ def accept_rejection(logits, drafts, u, temperature: float = 1.0, q=None, with_m
     if rc:
         raise ValueError("temperature must be > 0")
     return (out, mg) if with_margin else out
+
+
+# ---------------------------------------------------------------- layer chain
+def chain_pass(layers, x0, hidden: int, ffn: int, head=None, eps: float = 1e-6, threads=None):
+    """Plain reading of the verification pass over a projection stack.
+
+    layers: list of dicts with 'q','k','v','o','gate','up','down' ->
+    (qtype, GGUF bytes) and 'g1'..'g4' -> fp32 norm weights; head: None or
+    (qtype, GGUF bytes, gamma_final).  Per layer (the producer requantises
+    the next input including the next norm's weight; the RMS factor r of the
+    normalised vector multiplies the consumer's output):
+        a = Q8A32(x*g1);  q,k,v = r(x) W a;  b = Q8A32(v*g2);  o = r(v) Wo b;
+        c = Q8A32(o*g3);  g,u = r(o) W c;    h = Q8A32((g*u)*g4);
+        x = r(g*u) Wd h
+    Projections are fp64; every quantiser input is the fp32 rounding of the
+    fp64 value (the codes are fp32 decisions).  Returns (x_last fp64 [M,H],
+    logits fp64 [M,V] or None)."""
+    H, F = hidden, ffn
+
+    def fold(v64, gamma, n):
+        v32 = np.asarray(v64, np.float64).astype(np.float32)
+        q, d, _, ss = quantize_act(v32, gamma)
+        return q, d, rms_factor(ss, n, eps)
+
+    x = np.asarray(x0, np.float64)
+    for lw in layers:
+        q, d, r = fold(x, lw["g1"], H)
+        mv = lambda name, q=q, d=d, r=r, K=H: matvec(lw[name][0], lw[name][1], K, q, d, scale=r,
+                                                     threads=threads)[0]
+        mv("q")
+        mv("k")
+        v = mv("v")
+        q, d, r = fold(v, lw["g2"], H)
+        o = matvec(lw["o"][0], lw["o"][1], H, q, d, scale=r, threads=threads)[0]
+        q, d, r = fold(o, lw["g3"], H)
+        g = matvec(lw["gate"][0], lw["gate"][1], H, q, d, scale=r, threads=threads)[0]
+        u = matvec(lw["up"][0], lw["up"][1], H, q, d, scale=r, threads=threads)[0]
+        p = (g.astype(np.float32) * u.astype(np.float32)).astype(np.float64)
+        q, d, r = fold(p, lw["g4"], F)
+        x = matvec(lw["down"][0], lw["down"][1], F, q, d, scale=r, threads=threads)[0]
+    logits = None
+    if head is not None:
+        hq, hraw, gf = head
+        q, d, r = fold(x, gf, H)
+        logits = matvec(hq, hraw, H, q, d, scale=r, threads=threads)[0]
+    return x, logits

@@ -23,8 +23,10 @@ MAX_M = 16
 
 EXPORTS = [
     "sv_last_error", "sv_version", "sv_repacked_bytes", "sv_repack_weights", "sv_unpack_weights",
-    "sv_quantize_act_q8", "sv_verify_matvec", "sv_head_logits", "sv_argmax_index",
-    "sv_accept_greedy", "sv_accept_workspace_bytes", "sv_accept_rejection",
+    "sv_quantize_act_q8", "sv_matvec_workspace_bytes", "sv_verify_matvec", "sv_head_workspace_bytes",
+    "sv_head_logits", "sv_argmax_index", "sv_pass_workspace_bytes", "sv_pass_create", "sv_pass_run",
+    "sv_pass_status", "sv_pass_trace", "sv_pass_destroy", "sv_accept_greedy", "sv_accept_workspace_bytes",
+    "sv_accept_rejection",
 ]
 
 
@@ -51,6 +53,12 @@ class Epilogue(ctypes.Structure):
                 ("sumsq", ctypes.c_void_p)]
 
 
+class Phase(ctypes.Structure):
+    _fields_ = [("W", ctypes.POINTER(Weight)), ("n_w", ctypes.c_int32), ("A", Act),
+                ("y", ctypes.c_void_p * 3), ("ep", Epilogue), ("row_ids", ctypes.c_void_p),
+                ("n_rows", ctypes.c_int64), ("argmax", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -70,9 +78,24 @@ def lib():
         L.sv_repack_weights.argtypes = [i32, P, P, i64, i64, P]
         L.sv_unpack_weights.argtypes = [i32, P, P, i64, i64, P]
         L.sv_quantize_act_q8.argtypes = [P, i32, i64, P, P, P, P, P, P]
+        L.sv_matvec_workspace_bytes.restype = ctypes.c_size_t
+        L.sv_matvec_workspace_bytes.argtypes = [ctypes.POINTER(Weight), i32, ctypes.POINTER(Act)]
         L.sv_verify_matvec.argtypes = [ctypes.POINTER(Weight), i32, ctypes.POINTER(Act),
-                                       ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(Epilogue), P]
-        L.sv_head_logits.argtypes = [ctypes.POINTER(Weight), ctypes.POINTER(Act), P, i64, P, P, P]
+                                       ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(Epilogue), P,
+                                       ctypes.c_size_t, P]
+        L.sv_head_workspace_bytes.restype = ctypes.c_size_t
+        L.sv_head_workspace_bytes.argtypes = [ctypes.POINTER(Weight), ctypes.POINTER(Act), i64]
+        L.sv_head_logits.argtypes = [ctypes.POINTER(Weight), ctypes.POINTER(Act), P, i64, P, P, P,
+                                     ctypes.c_size_t, P]
+        L.sv_pass_workspace_bytes.restype = ctypes.c_size_t
+        L.sv_pass_workspace_bytes.argtypes = [ctypes.POINTER(Phase), i32]
+        L.sv_pass_create.argtypes = [ctypes.POINTER(Phase), i32, P, ctypes.c_size_t, ctypes.POINTER(P)]
+        L.sv_pass_run.argtypes = [P, P]
+        L.sv_pass_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
+        L.sv_pass_trace.restype = ctypes.c_int
+        L.sv_pass_trace.argtypes = [P, ctypes.c_int, P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32)]
+        L.sv_pass_destroy.restype = None
+        L.sv_pass_destroy.argtypes = [P]
         L.sv_argmax_index.restype = i64
         L.sv_argmax_index.argtypes = [ctypes.c_uint64]
         L.sv_accept_greedy.argtypes = [P, P, P, i32, P, P]
@@ -80,7 +103,8 @@ def lib():
         L.sv_accept_workspace_bytes.argtypes = [i64, i32]
         L.sv_accept_rejection.argtypes = [P, i64, P, P, i32, P, ctypes.c_float, P, ctypes.c_size_t, P, P]
         for f in ("sv_repack_weights", "sv_unpack_weights", "sv_quantize_act_q8", "sv_verify_matvec",
-                  "sv_head_logits", "sv_accept_greedy", "sv_accept_rejection"):
+                  "sv_head_logits", "sv_accept_greedy", "sv_accept_rejection", "sv_pass_create",
+                  "sv_pass_run", "sv_pass_status"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -138,18 +162,116 @@ def epilogue(mode, q, d, s16, sumsq, gamma=None, src=0) -> Epilogue:
                     s16.data_ptr(), sumsq.data_ptr())
 
 
-def verify_matvec(weights, A: Act, ys, ep: Epilogue | None = None, stream=None):
+_ws = {}
+
+
+def workspace(nbytes: int):
+    """A zero-filled, 256-byte aligned device scratch buffer of at least
+    nbytes, shared by the single-phase calls of this process (the library
+    leaves it zero-filled after every call)."""
+    import torch
+    dev = torch.cuda.current_device()
+    buf = _ws.get(dev)
+    if nbytes == 0:
+        return None
+    if buf is None or buf.numel() < nbytes + 256:
+        buf = torch.zeros(max(nbytes, 1 << 20) + 256, dtype=torch.uint8, device="cuda")
+        _ws[dev] = buf
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes]
+
+
+def _ws_args(nbytes, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = workspace(nbytes)
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def verify_matvec(weights, A: Act, ys, ep: Epilogue | None = None, workspace_buf=None, stream=None):
     n = len(weights)
     W = (Weight * n)(*weights)
     Y = (ctypes.c_void_p * n)(*[None if y is None else y.data_ptr() for y in ys])
-    _check(lib().sv_verify_matvec(W, n, ctypes.byref(A), Y, None if ep is None else ctypes.byref(ep),
+    need = lib().sv_matvec_workspace_bytes(W, n, ctypes.byref(A))
+    wp, wn = _ws_args(need, workspace_buf)
+    _check(lib().sv_verify_matvec(W, n, ctypes.byref(A), Y, None if ep is None else ctypes.byref(ep), wp, wn,
                                   _stream(stream)))
 
 
-def head_logits(H: Weight, A: Act, logits=None, argmax=None, row_ids=None, n_rows=None, stream=None):
+def head_logits(H: Weight, A: Act, logits=None, argmax=None, row_ids=None, n_rows=None, workspace_buf=None,
+                stream=None):
     n = H.rows if row_ids is None else (n_rows if n_rows is not None else row_ids.numel())
+    need = lib().sv_head_workspace_bytes(ctypes.byref(H), ctypes.byref(A), 0 if row_ids is None else n)
+    wp, wn = _ws_args(need, workspace_buf)
     _check(lib().sv_head_logits(ctypes.byref(H), ctypes.byref(A), _ptr(row_ids), n, _ptr(logits), _ptr(argmax),
-                                _stream(stream)))
+                                wp, wn, _stream(stream)))
+
+
+def phase(weights, A: Act, ys=(), ep: Epilogue | None = None, row_ids=None, n_rows=0, argmax=None) -> Phase:
+    """Descriptor of one phase of a whole-pass launch (see Pass)."""
+    n = len(weights)
+    ph = Phase()
+    arr = (Weight * n)(*weights)
+    ph._keep = arr
+    ph.W = ctypes.cast(arr, ctypes.POINTER(Weight))
+    ph.n_w = n
+    ph.A = A
+    for i, y in enumerate(list(ys)[:3]):
+        ph.y[i] = None if y is None else y.data_ptr()
+    if ep is not None:
+        ph.ep = ep
+    ph.row_ids = None if row_ids is None else row_ids.data_ptr()
+    ph.n_rows = int(n_rows if row_ids is not None else 0)
+    ph.argmax = None if argmax is None else argmax.data_ptr()
+    return ph
+
+
+class Pass:
+    """A chain of phases run as one persistent launch (sv_pass_*)."""
+
+    def __init__(self, phases):
+        import torch
+        n = len(phases)
+        arr = (Phase * n)(*phases)
+        self._phases = (arr, phases)
+        need = lib().sv_pass_workspace_bytes(arr, n)
+        if need == 0:
+            raise SpecVerifyError(SV_ERR_ARG, lib().sv_last_error().decode())
+        buf = torch.zeros(need + 256, dtype=torch.uint8, device="cuda")
+        off = (-buf.data_ptr()) % 256
+        self._ws = buf[off:off + need]
+        h = ctypes.c_void_p()
+        _check(lib().sv_pass_create(arr, n, ctypes.c_void_p(self._ws.data_ptr()), need, ctypes.byref(h)))
+        self._h = h
+
+    def run(self, stream=None):
+        _check(lib().sv_pass_run(self._h, _stream(stream)))
+
+    def status(self) -> int:
+        v = ctypes.c_uint32()
+        _check(lib().sv_pass_status(self._h, ctypes.byref(v)))
+        return v.value
+
+    def trace(self, enable=True):
+        """Enable per-phase timestamps for later runs; returns the grid size."""
+        g = ctypes.c_int32()
+        _check(lib().sv_pass_trace(self._h, int(enable), None, 0, ctypes.byref(g)))
+        return g.value
+
+    def read_trace(self, n_phases):
+        """[grid, n_phases, 4] uint64 record of the last traced run."""
+        import numpy as np
+        g = ctypes.c_int32()
+        _check(lib().sv_pass_trace(self._h, 1, None, 0, ctypes.byref(g)))
+        buf = np.zeros((g.value, n_phases, 4), np.uint64)
+        _check(lib().sv_pass_trace(self._h, 1, buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes, None))
+        return buf
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.sv_pass_destroy(self._h)
+            self._h = None
 
 
 def argmax_index(packed: int) -> int:

@@ -1,65 +1,85 @@
 // matvec.hip - the verification projection (a3), its fused producer
-// epilogue (a4) and the output head with fused argmax (a6, a9).
+// epilogue (a4), the output head with fused argmax (a6, a9) and the phase
+// sequencing of a whole pass in one persistent launch (a5).
 //
 // One weight stream serves all M positions ("Inside OpenJet Engine: making
 // speculative decoding pay", section "One GPU launch for a speculative
-// cycle": weight reads serve multiple verification positions, and
-// activation loads are reused across weight rows).
+// cycle": weight reads serve multiple verification positions, activation
+// loads are reused across weight rows, and one launch carries the phases of
+// a cycle separated by grid-wide synchronisation).
 //
-// Work mapping (one 256-thread workgroup = 4 waves per row tile):
-//  * The K axis is cut into 32-element sub-blocks.  A group of g lanes
-//    (g = 32 or 16, fixed by K alone) shares one row; lane j of the group
-//    takes sub-blocks j, j+g, j+2g, ... so g lanes read g consecutive 16-byte
-//    records of the row: one contiguous, aligned run per group.
-//  * Each lane carries R = 4 rows (row slots).  The activations of its
-//    sub-block are read from LDS once per step and reused for all R rows;
-//    the weights are read from HBM once and reused for all M positions.
-//  * Integer block sums come from v_dot4 (exact); the fp32 combine of a
-//    block is a fixed sequence of operations per (row, position); a lane
-//    accumulates its blocks in increasing order, then the g lanes of a group
-//    are combined by a butterfly.  None of this depends on M, so a row's
-//    result is bit-identical whatever else is in the batch.
-//  * Weights for the next step are loaded while the current step computes.
+// Work decomposition.  A phase (one or up to three matrices sharing an
+// input) is cut into units = (row tile, K chunk, matrix):
+//  * K is cut into 32-element sub-blocks.  A group of g lanes (g = 32 or
+//    16, fixed by K alone) shares one row; lane j of the group takes
+//    sub-blocks j, j+g, j+2g, ... of the chunk, so g lanes read g
+//    consecutive 16-byte records of a row: one contiguous aligned run.
+//  * Each lane carries R = 4 rows.  The activations of its sub-block are
+//    read from LDS once per step and reused for the R rows; the weights are
+//    read from HBM once and reused for all M positions.
+//  * A row tile has 64/g * 4 waves * R rows (32 or 64); the K axis is split
+//    into S(K) chunks so that even the smallest phases offer hundreds of
+//    units to the 256 compute units.
+// Arithmetic.  Integer block sums come from v_dot4 (exact); each block's
+// fp32 combine is a fixed sequence of operations per (row, position); a lane
+// adds its blocks in increasing order, the g lanes of a group are combined by
+// a butterfly, and the S chunk partials are added in chunk order by the last
+// unit of the row tile to finish.  Nothing depends on M or on which
+// workgroup ran which unit, so every output row is bit-identical to the same
+// row computed alone, and runs are deterministic.
+// Scheduling.  Single calls launch one workgroup per unit.  A whole pass
+// runs as one persistent launch sized to the number of workgroups the GPU
+// holds at once: the units of each phase are dealt round-robin, and a
+// workgroup issues a unit's first weight loads before it waits until the
+// phase its input comes from has finished.  All waits are bounded.
 #include <algorithm>
+#include <vector>
 
 #include "sv_internal.h"
 
 namespace sv {
 
-constexpr int kThreads = 256;
-constexpr int kR = 4;
-constexpr int kLdsBudget = 64 * 1024;
+constexpr int kThreads = 256;          // four waves
+constexpr int kR = 4;                  // rows per lane
+constexpr int kRows = 32;              // rows per tile: 8 groups of 8 lanes x 4 rows
+constexpr int kActRec = 32 + 4 + 8;     // LDS bytes per position per staged sub-block
+constexpr int kMaxChunkSteps = 12;      // most 256-element steps of K one unit covers
+constexpr int kMaxWaveSteps = 3;        // = kMaxChunkSteps / 4 waves
+constexpr int kMaxS = 8;                // most K chunks (K <= 24576)
+constexpr unsigned kSpinLimit = 1u << 22;
+constexpr int kMaxGrid = 1024;          // most workgroups a pass launches
 
-struct MvArgs {
+// Device-side description of one phase.
+struct PhaseDesc {
     const uint8_t *w[3];
-    int n_w;
-    int64_t N;      // output rows (tile space)
-    int64_t K;      // input features
-    int64_t wrows;  // rows of the stored matrix (stream strides)
-    size_t o1, o2, o3;
+    int32_t qtype, n_w;
+    int32_t N, K, wrows;
+    int32_t S, steps, n_tiles, per_tile, n_units, chunk_sub;
+    uint64_t o1, o2, o3;
     const int32_t *row_ids;
     const int8_t *aq;
     const float *ad;
     const int32_t *as16;
     const float *in_parts;
-    int n_parts;
+    int32_t n_parts;
     float eps;
     float *y[3];
-    int ep_mode, ep_src;
+    int32_t ep_mode, ep_src;
     const float *gamma;
     int8_t *oq;
     float *od;
     int32_t *os16;
     float *osumsq;
     unsigned long long *argmax;
-    int chunk_sub;
-    int n_tiles;
+    float *partial;           // [n_w][S][M][N] when S * n_w > 1
+    unsigned *tile_count;     // [n_tiles], zero between calls
+    unsigned *ready;          // finished row tiles of this phase (persistent mode)
+    const unsigned *wait;     // finished row tiles of the input's producer
+    uint32_t wait_target;
+    uint32_t unit_base;       // units of all earlier phases (persistent mode)
 };
 
-// Bytes of LDS per position per staged sub-block: 32 codes, fp32 scale, and
-// 8 bytes of per-format activation sums.
-constexpr int kActRec = 32 + 4 + 8;
-
+// ------------------------------------------------------------ weights
 template <int QT>
 struct WRaw;
 template <>
@@ -91,21 +111,21 @@ __device__ __forceinline__ uint2 ld_stream8(const uint8_t *p) {
 }
 
 template <int QT>
-__device__ __forceinline__ void load_w(WRaw<QT> &r, const uint8_t *__restrict__ w, const MvArgs &a, int64_t row,
+__device__ __forceinline__ void load_w(WRaw<QT> &r, const uint8_t *__restrict__ w, const PhaseDesc &P, int64_t row,
                                        int64_t s) {
-    const int64_t nsub = a.K >> 5;
+    const int64_t K = P.K, nsub = K >> 5;
     if constexpr (QT == SV_Q8_0) {
-        r.q0 = ld_stream16(w + row * a.K + s * 32);
-        r.q1 = ld_stream16(w + row * a.K + s * 32 + 16);
-        r.d = *reinterpret_cast<const uint16_t *>(w + a.o1 + (row * nsub + s) * 2);
+        r.q0 = ld_stream16(w + row * K + s * 32);
+        r.q1 = ld_stream16(w + row * K + s * 32 + 16);
+        r.d = *reinterpret_cast<const uint16_t *>(w + P.o1 + (row * nsub + s) * 2);
     } else if constexpr (QT == SV_Q4_K) {
         r.q = ld_stream16(w + (row * nsub + s) * 16);
-        r.h = *reinterpret_cast<const uint4 *>(w + a.o1 + (row * (a.K >> 8) + (s >> 3)) * 16);
+        r.h = *reinterpret_cast<const uint4 *>(w + P.o1 + (row * (K >> 8) + (s >> 3)) * 16);
     } else {
         r.l = ld_stream16(w + (row * nsub + s) * 16);
-        r.h = ld_stream8(w + a.o1 + (row * nsub + s) * 8);
-        r.sc = *reinterpret_cast<const uint16_t *>(w + a.o2 + row * (a.K >> 4) + 2 * s);
-        r.d = *reinterpret_cast<const uint16_t *>(w + a.o3 + (row * (a.K >> 8) + (s >> 3)) * 2);
+        r.h = ld_stream8(w + P.o1 + (row * nsub + s) * 8);
+        r.sc = *reinterpret_cast<const uint16_t *>(w + P.o2 + row * (K >> 4) + 2 * s);
+        r.d = *reinterpret_cast<const uint16_t *>(w + P.o3 + (row * (K >> 8) + (s >> 3)) * 2);
     }
 }
 
@@ -113,7 +133,7 @@ __device__ __forceinline__ void load_w(WRaw<QT> &r, const uint8_t *__restrict__ 
 // codes in the activation's element order, plus the block's scale terms.
 struct WDec {
     uint32_t v[8];
-    float s0, s1;  // Q8_0: d; Q4_K: d*sc, dmin*m; Q6_K: d
+    float s0, s1;    // Q8_0: d; Q4_K: d*sc, dmin*m; Q6_K: d
     int32_t i0, i1;  // Q6_K: the two int8 sub-scales
 };
 
@@ -130,8 +150,8 @@ __device__ __forceinline__ void decode_w(WDec &o, const WRaw<QT> &r, int j8) {
             o.v[k] = q[k] & 0x0F0F0F0Fu;
             o.v[4 + k] = (q[k] >> 4) & 0x0F0F0F0Fu;
         }
-        // 6-bit sub-scale and min of sub-block j8 from the packed 12 bytes
-        // (header dwords y, z, w), see the Q4_K layout of ggml.
+        // 6-bit sub-scale and min of sub-block j8 from the 12 packed bytes
+        // (header dwords y, z, w) of the ggml Q4_K layout.
         const uint32_t sh = 8u * (j8 & 3);
         uint32_t sc, mn;
         if (j8 < 4) {
@@ -171,14 +191,13 @@ __device__ __forceinline__ void decode_w(WDec &o, const WRaw<QT> &r, int j8) {
 struct ARec {
     uint32_t v[8];
     float d;
-    float xf;       // Q4_K: fp32 sum of the 32 codes
-    int32_t x0, x1; // Q6_K: -32 * (sum of codes of each 16-half)
+    float xf;        // Q4_K: fp32 sum of the 32 codes
+    int32_t x0, x1;  // Q6_K: -32 * (sum of codes of each 16-element half)
 };
 
 // One block term for one (row slot, position), accumulated into acc.
 template <int QT>
 __device__ __forceinline__ float block_term(const WDec &w, const ARec &a, float acc) {
-    int32_t S = 0;
     if constexpr (QT == SV_Q6_K) {
         int32_t S0 = 0, S1 = 0;
 #pragma unroll
@@ -191,6 +210,7 @@ __device__ __forceinline__ float block_term(const WDec &w, const ARec &a, float 
         I += __mul24(w.i1, a.x1);
         return fmaf(w.s0 * a.d, static_cast<float>(I), acc);
     } else {
+        int32_t S = 0;
 #pragma unroll
         for (int k = 0; k < 8; k++) S = dot4(w.v[k], a.v[k], S);
         if constexpr (QT == SV_Q8_0) {
@@ -202,6 +222,8 @@ __device__ __forceinline__ float block_term(const WDec &w, const ARec &a, float 
     }
 }
 
+// LDS record of the staged activation chunk, per position: [CS] 16-byte low
+// halves, [CS] 16-byte high halves, [CS] fp32 scales, [CS] 8-byte sums.
 __device__ __forceinline__ void read_act(ARec &r, const uint8_t *act_m, int CS, int sl) {
     const uint4 lo = *reinterpret_cast<const uint4 *>(act_m + sl * 16);
     const uint4 hi = *reinterpret_cast<const uint4 *>(act_m + CS * 16 + sl * 16);
@@ -214,213 +236,488 @@ __device__ __forceinline__ void read_act(ARec &r, const uint8_t *act_m, int CS, 
     r.xf = __int_as_float(x.x);
 }
 
-// Stage sub-blocks [s0, s0 + cs) of every position into LDS.
-template <int QT, int M>
-__device__ void stage_act(uint8_t *act, const MvArgs &a, int64_t s0, int cs, int CS) {
-    const int64_t K = a.K, nsub = K >> 5;
-    const int nhalf = M * cs * 2;
-    for (int i = threadIdx.x; i < nhalf; i += kThreads) {
-        const int m = i / (cs * 2), r = i % (cs * 2), sl = r >> 1, h = r & 1;
-        const uint4 v = *reinterpret_cast<const uint4 *>(a.aq + m * K + (s0 + sl) * 32 + h * 16);
-        *reinterpret_cast<uint4 *>(act + m * CS * kActRec + h * CS * 16 + sl * 16) = v;
-    }
-    for (int i = threadIdx.x; i < M * cs; i += kThreads) {
-        const int m = i / cs, sl = i % cs;
-        uint8_t *am = act + m * CS * kActRec;
-        reinterpret_cast<float *>(am + CS * 32)[sl] = a.ad[m * nsub + s0 + sl];
-        const int2 s = *reinterpret_cast<const int2 *>(a.as16 + m * (K >> 4) + 2 * (s0 + sl));
-        int2 x;
-        if constexpr (QT == SV_Q4_K) {
-            x.x = __float_as_int(static_cast<float>(s.x + s.y));
-            x.y = 0;
-        } else {
-            x.x = -32 * s.x;
-            x.y = -32 * s.y;
+// Shared state of a workgroup.
+template <int M>
+struct Shared {
+    float rscale[SV_MAX_M];
+    unsigned long long best[SV_MAX_M];
+    int last;
+    unsigned abort;
+    unsigned long long t_wait;
+};
+
+// Cross-workgroup data of one launch (partial sums, the next phase's
+// activation, counters) moves through device-coherent accesses (sc1: written
+// through to, and read from, the level all XCDs share) instead of fences:
+// an agent-scope fence writes back or invalidates a whole L2, which is far
+// too costly once per unit.  Ordering comes from s_waitcnt before the
+// barrier that precedes each counter update.
+template <typename T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+    return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's memory operations have completed.
+__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Completion of a phase is counted in kSlots counters kSlotStride words
+// apart (unit u adds to slot u % kSlots), so finishing units do not all
+// serialise on one address; a waiter sums the slots.
+constexpr int kSlots = 8;
+constexpr int kSlotStride = 64;
+
+__device__ bool wait_ready(const unsigned *ctr, unsigned target, unsigned *status, unsigned &abort_sh) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        unsigned n = 0;
+        bool ok = true;
+        for (;;) {
+            unsigned v = (lane < kSlots) ? ld_dev(ctr + lane * kSlotStride) : 0u;
+#pragma unroll
+            for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+            v = __shfl(v, 0, 64);
+            if (v >= target) break;
+            if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || ++n > kSpinLimit) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
         }
-        reinterpret_cast<int2 *>(am + CS * 36)[sl] = x;
+        if (lane == 0) {
+            if (!ok) atomicOr(status, 1u);
+            abort_sh = ok ? 0u : 1u;
+        }
+    }
+    __syncthreads();
+    return abort_sh == 0u;
+}
+
+// Stage positions [m0, m0 + mg) of the chunk's sub-blocks [s0, s0 + cs) into
+// LDS and, when rs is given, form the input's RMS factors in the same round
+// trip (lane-strided sequential sums over the partials, then a butterfly
+// over the wave: a fixed order that depends only on n_parts).  Every global
+// load of a thread is issued before the first one is used.
+constexpr int kStageHalf = 6;   // >= 8 positions * 96 sub-blocks * 2 halves / 256 threads
+constexpr int kStageRec = 3;    // >= 8 * 96 / 256
+constexpr int kPartsPerLane = 9;  // >= 544 partials / 64 lanes
+
+__device__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int64_t s0, int cs, int CS,
+                          float *rs, int M) {
+    const int64_t K = P.K, nsub = K >> 5;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // RMS partials: two positions per wave per round (positions wave + 4 k)
+    float pv[2][kPartsPerLane];
+    const bool do_rs = rs && P.in_parts;
+    if (do_rs) {
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const int m = wave + 4 * k;
+#pragma unroll
+            for (int j = 0; j < kPartsPerLane; j++) {
+                const int i = lane + 64 * j;
+                pv[k][j] = (m < M && i < P.n_parts) ? P.in_parts[m * P.n_parts + i] : 0.0f;
+            }
+        }
+    }
+    const int nhalf = mg * cs * 2, nrec = mg * cs;
+    uint4 hv[kStageHalf];
+    float dv[kStageRec];
+    int2 sv[kStageRec];
+#pragma unroll
+    for (int k = 0; k < kStageHalf; k++) {
+        const int i = threadIdx.x + k * kThreads;
+        if (i < nhalf) {
+            const int m = i / (cs * 2), r = i % (cs * 2), sl = r >> 1, h = r & 1;
+            hv[k] = *reinterpret_cast<const uint4 *>(P.aq + (m0 + m) * K + (s0 + sl) * 32 + h * 16);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kStageRec; k++) {
+        const int i = threadIdx.x + k * kThreads;
+        if (i < nrec) {
+            const int m = i / cs, sl = i % cs;
+            dv[k] = P.ad[(m0 + m) * nsub + s0 + sl];
+            sv[k] = *reinterpret_cast<const int2 *>(P.as16 + (m0 + m) * (K >> 4) + 2 * (s0 + sl));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kStageHalf; k++) {
+        const int i = threadIdx.x + k * kThreads;
+        if (i < nhalf) {
+            const int m = i / (cs * 2), r = i % (cs * 2), sl = r >> 1, h = r & 1;
+            *reinterpret_cast<uint4 *>(act + m * CS * kActRec + h * CS * 16 + sl * 16) = hv[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kStageRec; k++) {
+        const int i = threadIdx.x + k * kThreads;
+        if (i < nrec) {
+            const int m = i / cs, sl = i % cs;
+            uint8_t *am = act + m * CS * kActRec;
+            reinterpret_cast<float *>(am + CS * 32)[sl] = dv[k];
+            int2 x;
+            if (P.qtype == SV_Q4_K) {
+                x.x = __float_as_int(static_cast<float>(sv[k].x + sv[k].y));
+                x.y = 0;
+            } else {
+                x.x = -32 * sv[k].x;
+                x.y = -32 * sv[k].y;
+            }
+            reinterpret_cast<int2 *>(am + CS * 36)[sl] = x;
+        }
+    }
+    if (rs) {
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const int m = wave + 4 * k;
+            if (k == 2 && do_rs && M > 8) {
+                // positions 8..15: second round of partial loads
+#pragma unroll
+                for (int kk = 0; kk < 2; kk++) {
+                    const int mm = wave + 4 * (kk + 2);
+#pragma unroll
+                    for (int j = 0; j < kPartsPerLane; j++) {
+                        const int i = lane + 64 * j;
+                        pv[kk][j] = (mm < M && i < P.n_parts) ? P.in_parts[mm * P.n_parts + i] : 0.0f;
+                    }
+                }
+            }
+            if (m < M) {
+                float r = 1.0f;
+                if (do_rs) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < kPartsPerLane; j++) s += pv[k & 1][j];
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+                    r = 1.0f / sqrtf(s / static_cast<float>(P.K) + P.eps);
+                }
+                if (lane == 0) rs[m] = r;
+            }
+        }
     }
 }
 
-template <int QT, int M, int GL>
-__global__ __launch_bounds__(kThreads) void mv_kernel(MvArgs a) {
-    constexpr int g = 1 << GL, G = 64 >> GL;
-    constexpr int ROWS = 4 * G * kR;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int grp = lane >> GL, jl = lane & (g - 1);
-    const int j8 = jl & 7;
-    const int64_t nsub = a.K >> 5;
-    const int CS = a.chunk_sub;
-    const int nchunks = static_cast<int>((nsub + CS - 1) / CS);
-
-    extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t *act = smem;
-    float *ystage = reinterpret_cast<float *>(smem + M * CS * kActRec);
-    float *rscale = ystage + a.n_w * M * ROWS;
-    unsigned long long *bestbuf = reinterpret_cast<unsigned long long *>(rscale + SV_MAX_M);
-
-    // RMS factor of the input (fixed order: lane-strided sequential sums,
-    // then a butterfly over the wave).
-    for (int m = wave; m < M; m += 4) {
-        float r = 1.0f;
-        if (a.in_parts) {
-            float s = 0.0f;
-            for (int i = lane; i < a.n_parts; i += 64) s += a.in_parts[m * a.n_parts + i];
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-            r = 1.0f / sqrtf(s / static_cast<float>(a.K) + a.eps);
+// Epilogue of a finished row tile (LDS ystage [n_w][M][kRows]): y outputs
+// of the matrices in [mat_lo, mat_hi), argmax candidates and the requantised
+// next activation.
+template <int M>
+__device__ void finish_tile(const PhaseDesc &P, const float *ystage, int64_t row0, int mat_lo, int mat_hi,
+                            bool do_ep, Shared<M> &sh) {
+    const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), static_cast<int64_t>(P.N) - row0));
+    for (int mat = mat_lo; mat < mat_hi; mat++) {
+        float *y = P.y[mat];
+        if (!y) continue;
+        for (int i = threadIdx.x; i < M * kRows; i += kThreads) {
+            const int m = i / kRows, r = i % kRows;
+            if (r < rows_here) y[static_cast<int64_t>(m) * P.N + row0 + r] = ystage[(mat * M + m) * kRows + r];
         }
-        if (lane == 0) rscale[m] = r;
     }
-
-    unsigned long long best[M];
-#pragma unroll
-    for (int m = 0; m < M; m++) best[m] = 0ull;
-
-    bool staged_once = false;
-    for (int tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
-        const int64_t row0 = static_cast<int64_t>(tile) * ROWS;
-        const int slot0 = (wave * G + grp) * kR;
-        for (int mat = 0; mat < a.n_w; mat++) {
-            const uint8_t *__restrict__ w = a.w[mat];
-            int64_t srow[kR];
-#pragma unroll
-            for (int p = 0; p < kR; p++) {
-                int64_t rr = row0 + slot0 + p;
-                if (rr >= a.N) rr = 0;
-                int64_t sr = a.row_ids ? static_cast<int64_t>(a.row_ids[rr]) : rr;
-                // Out-of-range ids are a caller error; clamp so no read
-                // leaves the matrix.
-                srow[p] = (sr < 0 || sr >= a.wrows) ? 0 : sr;
-            }
-            float acc[kR][M];
-#pragma unroll
-            for (int p = 0; p < kR; p++)
-#pragma unroll
-                for (int m = 0; m < M; m++) acc[p][m] = 0.0f;
-
-            for (int c = 0; c < nchunks; c++) {
-                const int64_t s0 = static_cast<int64_t>(c) * CS;
-                const int cs = static_cast<int>(std::min<int64_t>(CS, nsub - s0));
-                if (nchunks > 1 || !staged_once) {
-                    __syncthreads();
-                    stage_act<QT, M>(act, a, s0, cs, CS);
-                    __syncthreads();
-                    staged_once = true;
-                }
-                const int T = (cs + g - 1) / g;
-                WRaw<QT> raw[kR];
-                if (jl < cs) {
-#pragma unroll
-                    for (int p = 0; p < kR; p++) load_w<QT>(raw[p], w, a, srow[p], s0 + jl);
-                }
-                for (int t = 0; t < T; t++) {
-                    const int sl = jl + g * t;
-                    const bool valid = sl < cs;
-                    WDec dec[kR];
-                    if (valid) {
-#pragma unroll
-                        for (int p = 0; p < kR; p++) decode_w<QT>(dec[p], raw[p], j8);
-                    }
-                    if (sl + g < cs) {
-#pragma unroll
-                        for (int p = 0; p < kR; p++) load_w<QT>(raw[p], w, a, srow[p], s0 + sl + g);
-                    }
-                    if (valid) {
-#pragma unroll
-                        for (int m = 0; m < M; m++) {
-                            ARec ar;
-                            read_act(ar, act + m * CS * kActRec, CS, sl);
-#pragma unroll
-                            for (int p = 0; p < kR; p++) acc[p][m] = block_term<QT>(dec[p], ar, acc[p][m]);
-                        }
-                    }
-                }
-            }
-            // Combine the g lanes of each group (butterfly; all lanes end
-            // with the same value) and stage the scaled result.
-#pragma unroll
-            for (int p = 0; p < kR; p++)
-#pragma unroll
-                for (int m = 0; m < M; m++) {
-                    float v = acc[p][m];
-#pragma unroll
-                    for (int o = g >> 1; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-                    acc[p][m] = v;
-                }
-            if (jl == 0) {
-#pragma unroll
-                for (int p = 0; p < kR; p++)
-#pragma unroll
-                    for (int m = 0; m < M; m++) ystage[(mat * M + m) * ROWS + slot0 + p] = acc[p][m] * rscale[m];
-            }
-        }
-        __syncthreads();
-        const int rows_here = static_cast<int>(std::min<int64_t>(ROWS, a.N - row0));
-        // Outputs, coalesced.
-        for (int mat = 0; mat < a.n_w; mat++) {
-            if (!a.y[mat]) continue;
-            for (int i = threadIdx.x; i < M * ROWS; i += kThreads) {
-                const int m = i / ROWS, r = i % ROWS;
-                if (r < rows_here) a.y[mat][m * a.N + row0 + r] = ystage[(mat * M + m) * ROWS + r];
-            }
-        }
-        // Fused argmax over this tile's rows.
-        if (a.argmax) {
-            for (int m = 0; m < M; m++) {
-                unsigned long long b = 0ull;
-                for (int r = threadIdx.x; r < rows_here; r += kThreads)
-                        b = umax64(b, pack_argmax(ystage[m * ROWS + r], static_cast<uint32_t>(row0 + r)));
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) b = umax64(b, __shfl_xor(b, o, 64));
-                best[m] = umax64(best[m], b);
-            }
-        }
-        // Fused requantisation for the next consumer.
-        if (a.ep_mode != SV_EP_NONE) {
-            const int nblk = rows_here / 32;
-            const int hw = threadIdx.x >> 5, l32 = threadIdx.x & 31;
-            for (int it = hw; it < M * nblk; it += kThreads / 32) {
-                const int m = it / nblk, blk = it % nblk;
-                const int r = blk * 32 + l32;
-                float v;
-                if (a.ep_mode == SV_EP_PAIR) v = ystage[(0 * M + m) * ROWS + r] * ystage[(1 * M + m) * ROWS + r];
-                else v = ystage[(a.ep_src * M + m) * ROWS + r];
-                const int64_t grow = row0 + r;
-                const float vg = a.gamma ? v * a.gamma[grow] : v;
-                float am = fabsf(vg);
-#pragma unroll
-                for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
-                const float dd = am / 127.0f;
-                const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
-                float rq = roundf(vg * id);
-                rq = fminf(fmaxf(rq, -127.0f), 127.0f);
-                const int qi = static_cast<int>(rq);
-                a.oq[m * a.N + grow] = static_cast<int8_t>(qi);
-                int s = qi;
-#pragma unroll
-                for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 32);
-                float sq = v * v;
-#pragma unroll
-                for (int o = 16; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 32);
-                const int64_t gb = grow >> 5;
-                if ((l32 & 15) == 0) a.os16[m * (a.N >> 4) + 2 * gb + (l32 >> 4)] = s;
-                if (l32 == 0) {
-                    a.od[m * (a.N >> 5) + gb] = dd;
-                    a.osumsq[m * (a.N >> 5) + gb] = sq;
-                }
-            }
-        }
-        __syncthreads();
-    }
-    if (a.argmax) {
+    if (P.argmax) {
+        const int lane = threadIdx.x & 63;
         for (int m = 0; m < M; m++) {
-            if (lane == 0) bestbuf[wave * SV_MAX_M + m] = best[m];
-        }
-        __syncthreads();
-        if (threadIdx.x < M) {
             unsigned long long b = 0ull;
-            for (int wv = 0; wv < 4; wv++) b = umax64(b, bestbuf[wv * SV_MAX_M + threadIdx.x]);
-            if (b) atomicMax(a.argmax + threadIdx.x, b);
+            for (int r = threadIdx.x; r < rows_here; r += kThreads)
+                b = umax64(b, pack_argmax(ystage[m * kRows + r], static_cast<uint32_t>(row0 + r)));
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) b = umax64(b, __shfl_xor(b, o, 64));
+            if (lane == 0 && b) atomicMax(&sh.best[m], b);
+        }
+    }
+    if (do_ep && P.ep_mode != SV_EP_NONE && rows_here == kRows) {
+        const int hw = threadIdx.x >> 5, l32 = threadIdx.x & 31;
+        const int64_t N = P.N;
+        for (int m = hw; m < M; m += kThreads / 32) {
+            float v;
+            if (P.ep_mode == SV_EP_PAIR) v = ystage[(0 * M + m) * kRows + l32] * ystage[(1 * M + m) * kRows + l32];
+            else v = ystage[(P.ep_src * M + m) * kRows + l32];
+            const int64_t grow = row0 + l32;
+            const float vg = P.gamma ? v * P.gamma[grow] : v;
+            float am = fabsf(vg);
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+            const float dd = am / 127.0f;
+            const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
+            float rq = roundf(vg * id);
+            rq = fminf(fmaxf(rq, -127.0f), 127.0f);
+            const int qi = static_cast<int>(rq);
+            st_dev(P.oq + m * N + grow, static_cast<int8_t>(qi));
+            int s = qi;
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 32);
+            float sq = v * v;
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 32);
+            const int64_t gb = grow >> 5;
+            if ((l32 & 15) == 0) st_dev(P.os16 + m * (N >> 4) + 2 * gb + (l32 >> 4), s);
+            if (l32 == 0) {
+                st_dev(P.od + m * (N >> 5) + gb, dd);
+                st_dev(P.osumsq + m * (N >> 5) + gb, sq);
+            }
+        }
+    }
+}
+
+// Positions staged in LDS at once (two rounds for M > 8; the raw weights
+// stay in registers, so nothing is read twice from memory).
+template <int M>
+struct MG {
+    static constexpr int value = M > 8 ? 8 : M;
+};
+
+// One unit: rows [row0, row0 + 32) x the K chunk `chunk`, for matrices
+// [mat_lo, mat_hi).  Wave w takes steps [w0, w1) of the chunk (one step = 8
+// sub-blocks per row, one 256-element super-block of a K-quant); lane j of
+// row group grp reads sub-block 8 t + j of rows row0 + 4 grp + p, p < 4.
+template <int QT, int M>
+__device__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart, int CS,
+                         Shared<M> &sh, bool do_wait, unsigned *status) {
+    constexpr int MGV = MG<M>::value;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 3, jl = lane & 7;
+    const bool pair = P.ep_mode == SV_EP_PAIR;
+    const int per_tile = P.per_tile;
+    const int tile = unit / per_tile;
+    const int rem = unit % per_tile;
+    const int chunk = rem % P.S;
+    const int mat = rem / P.S;
+    const int64_t row0 = static_cast<int64_t>(tile) * kRows;
+    const int64_t nsub = P.K >> 5;
+    const int c0 = static_cast<int>(static_cast<int64_t>(chunk) * P.steps / P.S);
+    const int c1 = static_cast<int>(static_cast<int64_t>(chunk + 1) * P.steps / P.S);
+    const int tc = c1 - c0;
+    const int w0 = c0 + wave * tc / 4, w1 = c0 + (wave + 1) * tc / 4;
+    const int64_t s_begin = static_cast<int64_t>(c0) * 8;
+    const int cs = static_cast<int>(min(static_cast<int64_t>(tc) * 8, nsub - s_begin));
+
+    int64_t srow[kR];
+#pragma unroll
+    for (int p = 0; p < kR; p++) {
+        int64_t rr = row0 + grp * kR + p;
+        if (rr >= P.N) rr = 0;
+        const int64_t sr = P.row_ids ? static_cast<int64_t>(P.row_ids[rr]) : rr;
+        // out-of-range ids are a caller error; clamp so no read leaves the matrix
+        srow[p] = (sr < 0 || sr >= P.wrows) ? 0 : sr;
+    }
+    // Every weight record of this unit is requested before waiting for the
+    // input (at most kMaxWaveSteps steps per wave).
+    const uint8_t *__restrict__ w = P.w[mat];
+    WRaw<QT> raw[kMaxWaveSteps][kR];
+#pragma unroll
+    for (int t = 0; t < kMaxWaveSteps; t++) {
+        const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
+        if (w0 + t < w1 && sb < nsub) {
+#pragma unroll
+            for (int p = 0; p < kR; p++) load_w<QT>(raw[t][p], w, P, srow[p], sb);
+        }
+    }
+    bool need_rs = false;
+    if (do_wait) {
+        if (P.wait && !wait_ready(P.wait, P.wait_target, status, sh.abort)) return false;
+        if (threadIdx.x == 0) sh.t_wait = __builtin_amdgcn_s_memrealtime();
+        need_rs = true;
+    }
+    float acc[kR][M];
+#pragma unroll
+    for (int p = 0; p < kR; p++)
+#pragma unroll
+        for (int m = 0; m < M; m++) acc[p][m] = 0.0f;
+#pragma unroll
+    for (int m0 = 0; m0 < M; m0 += MGV) {
+        const int mg = min(MGV, M - m0);
+        __syncthreads();
+        stage_act(act, P, m0, mg, s_begin, cs, CS, (need_rs && m0 == 0) ? sh.rscale : nullptr, M);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kMaxWaveSteps; t++) {
+            const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
+            if (w0 + t < w1 && sb < nsub) {
+                const int sl = static_cast<int>(sb - s_begin);
+                WDec dec[kR];
+#pragma unroll
+                for (int p = 0; p < kR; p++) decode_w<QT>(dec[p], raw[t][p], jl);
+#pragma unroll
+                for (int m = 0; m < MGV; m++) {
+                    if (m0 + m < M) {
+                        ARec ar;
+                        read_act(ar, act + m * CS * kActRec, CS, sl);
+#pragma unroll
+                        for (int p = 0; p < kR; p++) acc[p][m0 + m] = block_term<QT>(dec[p], ar, acc[p][m0 + m]);
+                    }
+                }
+            }
+        }
+    }
+    // Lanes of a row group: butterfly; waves: partials through LDS, added in
+    // wave order.
+#pragma unroll
+    for (int p = 0; p < kR; p++)
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            float v = acc[p][m];
+#pragma unroll
+            for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+            if (jl == 0) wpart[(wave * M + m) * kRows + grp * kR + p] = v;
+        }
+    __syncthreads();
+    // chunk value of (m, row) = ((w0 + w1) + w2) + w3.  A tile is final here
+    // unless K is split over units or the epilogue pairs two matrices.
+    const bool split = P.S > 1 || pair;
+    for (int i = threadIdx.x; i < M * kRows; i += kThreads) {
+        const int m = i / kRows, r = i % kRows;
+        float v = wpart[(0 * M + m) * kRows + r];
+        v += wpart[(1 * M + m) * kRows + r];
+        v += wpart[(2 * M + m) * kRows + r];
+        v += wpart[(3 * M + m) * kRows + r];
+        if (!split) {
+            ystage[(mat * M + m) * kRows + r] = v * sh.rscale[m];
+        } else {
+            const int64_t rr = row0 + r;
+            if (rr < P.N) st_dev(P.partial + ((static_cast<int64_t>(mat) * P.S + chunk) * M + m) * P.N + rr, v);
+        }
+    }
+    if (!split) {
+        __syncthreads();
+        finish_tile<M>(P, ystage, row0, mat, mat + 1, mat == P.ep_src, sh);
+        return true;
+    }
+    // K split over units: the last unit of the tile to finish adds the chunk
+    // partials in chunk order and runs the epilogue.
+    drain();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(P.tile_count + tile, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        sh.last = (prev == static_cast<unsigned>(per_tile - 1)) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!sh.last) return true;
+    const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), static_cast<int64_t>(P.N) - row0));
+    for (int i = threadIdx.x; i < P.n_w * M * kRows; i += kThreads) {
+        const int mt = i / (M * kRows), r2 = i % (M * kRows), m = r2 / kRows, r = r2 % kRows;
+        float s = 0.0f;
+        if (r < rows_here) {
+            const float *src = P.partial + (static_cast<int64_t>(mt) * P.S * M + m) * P.N + row0 + r;
+            float v[kMaxS];
+#pragma unroll
+            for (int c = 0; c < kMaxS; c++) v[c] = (c < P.S) ? ld_dev(src + static_cast<int64_t>(c) * M * P.N) : 0.0f;
+#pragma unroll
+            for (int c = 0; c < kMaxS; c++)
+                if (c < P.S) s += v[c];
+        }
+        ystage[(mt * M + m) * kRows + r] = s * sh.rscale[m];
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(P.tile_count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    finish_tile<M>(P, ystage, row0, 0, P.n_w, true, sh);
+    return true;
+}
+
+template <int M>
+__device__ __forceinline__ bool dispatch_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart,
+                                              int CS, Shared<M> &sh, bool do_wait, unsigned *status) {
+    if (P.qtype == SV_Q4_K) return run_unit<SV_Q4_K, M>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
+    if (P.qtype == SV_Q6_K) return run_unit<SV_Q6_K, M>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
+    return run_unit<SV_Q8_0, M>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
+}
+
+__device__ __forceinline__ void flush_best(const PhaseDesc &P, unsigned long long *best, int M) {
+    __syncthreads();
+    if (P.argmax && static_cast<int>(threadIdx.x) < M) {
+        if (best[threadIdx.x]) atomicMax(P.argmax + threadIdx.x, best[threadIdx.x]);
+        best[threadIdx.x] = 0ull;
+    }
+    __syncthreads();
+}
+
+// LDS layout of a workgroup: act chunk [MG][CS * kActRec] | ystage
+// [3][M][kRows] fp32 | wave partials [4][M][kRows] fp32.
+template <int M>
+__device__ __forceinline__ void lds_parts(uint8_t *smem, int CS, float *&ystage, float *&wpart) {
+    ystage = reinterpret_cast<float *>(smem + MG<M>::value * CS * kActRec);
+    wpart = ystage + 3 * M * kRows;
+}
+
+// One workgroup per unit of a single phase.
+template <int M>
+__global__ __launch_bounds__(kThreads) void phase_kernel(PhaseDesc P, int CS) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ Shared<M> sh;
+    float *ystage, *wpart;
+    lds_parts<M>(smem, CS, ystage, wpart);
+    if (threadIdx.x < SV_MAX_M) sh.best[threadIdx.x] = 0ull;
+    dispatch_unit<M>(P, blockIdx.x, smem, ystage, wpart, CS, sh, true, nullptr);
+    flush_best(P, sh.best, M);
+}
+
+// ctl: [1] status, [2] exited workgroups, then per phase kSlots counters of
+// finished units.  The last workgroup to exit returns every counter but the
+// status to zero, so the next run starts clean without a reset launch.
+template <int M>
+__global__ __launch_bounds__(kThreads) void pass_kernel(const PhaseDesc *__restrict__ table, int n_phases,
+                                                        unsigned *ctl, int CS, unsigned long long *argmax,
+                                                        unsigned long long *trace) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ Shared<M> sh;
+    __shared__ PhaseDesc P;
+    float *ystage, *wpart;
+    lds_parts<M>(smem, CS, ystage, wpart);
+    unsigned *status = ctl + 1;
+    if (threadIdx.x < SV_MAX_M) sh.best[threadIdx.x] = 0ull;
+    // Workgroup 0 clears the head's argmax: no head tile can finish before
+    // phase 0 has, and phase 0 needs workgroup 0's first unit.
+    if (blockIdx.x == 0 && argmax && static_cast<int>(threadIdx.x) < M) st_dev(argmax + threadIdx.x, 0ull);
+    const uint32_t G = gridDim.x, b = blockIdx.x;
+    int cur = -1;
+    bool ok = true;
+    for (int p = 0; p < n_phases && ok; p++) {
+        // units of phase p are dealt round-robin, continuing where phase
+        // p-1 stopped, so every workgroup gets its share of every phase
+        const uint32_t base = table[p].unit_base, nu = static_cast<uint32_t>(table[p].n_units);
+        uint32_t u = (b + G - base % G) % G;
+        if (u >= nu) continue;
+        if (cur >= 0) flush_best(P, sh.best, M);
+        if (threadIdx.x == 0) P = table[p];
+        __syncthreads();
+        cur = p;
+        bool first = true;
+        unsigned long long *tr = trace ? trace + (static_cast<size_t>(b) * n_phases + p) * 4 : nullptr;
+        if (tr && threadIdx.x == 0) tr[0] = __builtin_amdgcn_s_memrealtime();
+        unsigned n_done = 0;
+        for (; u < nu; u += G) {
+            ok = dispatch_unit<M>(P, static_cast<int>(u), smem, ystage, wpart, CS, sh, first, status);
+            if (!ok) break;
+            if (first && tr && threadIdx.x == 0) tr[1] = sh.t_wait;
+            first = false;
+            n_done++;
+            drain();
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                if (P.ready)
+                    __hip_atomic_fetch_add(P.ready + (u % kSlots) * kSlotStride, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                sh.last = 0;
+            }
+            __syncthreads();
+        }
+        if (tr && threadIdx.x == 0) {
+            tr[2] = __builtin_amdgcn_s_memrealtime();
+            tr[3] = n_done;
+        }
+    }
+    if (cur >= 0) flush_best(P, sh.best, M);
+    drain();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == gridDim.x - 1) {
+            for (int i = kSlotStride; i < kSlotStride * (1 + n_phases * kSlots); i += kSlotStride)
+                __hip_atomic_store(ctl + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ctl + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -430,46 +727,70 @@ __global__ void zero_u64(unsigned long long *p, int n) {
 }
 
 // ------------------------------------------------------------- dispatch
-using KernelFn = void (*)(MvArgs);
-
-template <int QT, int GL, int M>
-static KernelFn pick_m(int m) {
-    if constexpr (M > SV_MAX_M) {
-        return nullptr;
-    } else {
-        if (m == M) return mv_kernel<QT, M, GL>;
-        return pick_m<QT, GL, M + 1>(m);
+template <int MM = 1>
+static void launch_any(int M, bool pass, const PhaseDesc &P, const PhaseDesc *table, int n, unsigned *ctl, int grid,
+                       int CS, size_t lds, hipStream_t st, unsigned long long *am = nullptr,
+                       unsigned long long *tr = nullptr) {
+    if constexpr (MM <= SV_MAX_M) {
+        if (M != MM) {
+            launch_any<MM + 1>(M, pass, P, table, n, ctl, grid, CS, lds, st, am, tr);
+            return;
+        }
+        if (pass)
+            hipLaunchKernelGGL((pass_kernel<MM>), dim3(grid), dim3(kThreads), lds, st, table, n, ctl, CS, am, tr);
+        else
+            hipLaunchKernelGGL((phase_kernel<MM>), dim3(grid), dim3(kThreads), lds, st, P, CS);
     }
 }
 
-template <int QT>
-static KernelFn pick(int gl, int m) {
-    if (gl == 5) return pick_m<QT, 5, 1>(m);
-    return pick_m<QT, 4, 1>(m);
+template <int MM = 1>
+static int occupancy_any(int M, size_t lds) {
+    if constexpr (MM <= SV_MAX_M) {
+        if (M != MM) return occupancy_any<MM + 1>(M, lds);
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(&pass_kernel<MM>),
+                                                         kThreads, lds) != hipSuccess)
+            return 0;
+        return n;
+    }
+    return 0;
 }
 
-static KernelFn pick_kernel(int qt, int gl, int m) {
-    if (qt == SV_Q8_0) return pick<SV_Q8_0>(gl, m);
-    if (qt == SV_Q4_K) return pick<SV_Q4_K>(gl, m);
-    return pick<SV_Q6_K>(gl, m);
+// Decomposition of a phase: a function of K, rows and the matrix count only.
+static void decompose(PhaseDesc &P) {
+    const int64_t nsub = P.K / 32;
+    P.steps = static_cast<int>((nsub + 7) / 8);
+    P.S = std::max(1, (P.steps + kMaxChunkSteps - 1) / kMaxChunkSteps);
+    P.n_tiles = static_cast<int>((static_cast<int64_t>(P.N) + kRows - 1) / kRows);
+    P.per_tile = P.S * P.n_w;
+    P.n_units = P.n_tiles * P.per_tile;
+    P.chunk_sub = ((P.steps + P.S - 1) / P.S) * 8;
 }
 
-// Lanes per row group: 32 when the sub-block count allows a full-width
-// split, else 16.  A function of K only.
-static int group_log2(int64_t K) {
-    const int64_t nsub = K / 32;
-    return (nsub % 32 == 0) ? 5 : 4;
+static size_t lds_bytes(int M, int CS) {
+    const int mg = M > 8 ? 8 : M;
+    return static_cast<size_t>(mg) * CS * kActRec + static_cast<size_t>(3) * M * kRows * 4 +
+           static_cast<size_t>(4) * M * kRows * 4;
+}
+
+static bool needs_partials(const PhaseDesc &P) { return P.S > 1 || P.ep_mode == SV_EP_PAIR; }
+
+static size_t partial_bytes(const PhaseDesc &P, int M) {
+    if (!needs_partials(P)) return 0;
+    return static_cast<size_t>(P.n_w) * P.S * M * static_cast<size_t>(P.N) * 4;
 }
 
 static int validate_act(const sv_act *A) {
     SV_REQUIRE(A, SV_ERR_ARG, "activation descriptor is NULL");
     SV_REQUIRE(A->M >= 1 && A->M <= SV_MAX_M, SV_ERR_ARG, "M must be in [1, 16]");
     SV_REQUIRE(A->q && A->d && A->s16, SV_ERR_ARG, "activation buffers must not be NULL");
-    SV_REQUIRE(A->K > 0 && A->K % 32 == 0, SV_ERR_SHAPE, "activation K must be a positive multiple of 32");
+    SV_REQUIRE(A->K > 0 && A->K % 32 == 0 && A->K <= kMaxS * kMaxChunkSteps * 256, SV_ERR_SHAPE,
+               "activation K must be a positive multiple of 32, at most 24576");
     SV_REQUIRE(aligned(A->q, 16) && aligned(A->d, 4) && aligned(A->s16, 8), SV_ERR_ALIGN,
                "activation codes must be 16-byte aligned, scales 4-byte, sums 8-byte");
     if (A->sumsq_parts) {
-        SV_REQUIRE(A->n_parts >= 1, SV_ERR_ARG, "n_parts must be >= 1 when sumsq_parts is given");
+        SV_REQUIRE(A->n_parts >= 1 && A->n_parts <= kPartsPerLane * 64, SV_ERR_ARG,
+                   "n_parts must be in [1, 576] when sumsq_parts is given");
         SV_REQUIRE(aligned(A->sumsq_parts, 4), SV_ERR_ALIGN, "sumsq_parts must be 4-byte aligned");
     }
     return SV_OK;
@@ -488,126 +809,312 @@ static int validate_weight(const sv_weight &W, int64_t K) {
     return SV_OK;
 }
 
-static int launch(MvArgs &a, int qt, int M, int grid_cap, hipStream_t st) {
-    const int gl = group_log2(a.K);
-    const int g = 1 << gl;
-    const int rows_tile = 4 * (64 >> gl) * kR;
-    const int64_t nsub = a.K / 32;
-    const int fixed = a.n_w * M * rows_tile * 4 + SV_MAX_M * 4 + 4 * SV_MAX_M * 8;
-    int cs = static_cast<int>((kLdsBudget - fixed) / (M * kActRec));
-    cs = (cs / g) * g;
-    const int64_t nsub_r = (nsub + g - 1) / g * g;
-    if (cs > nsub_r) cs = static_cast<int>(nsub_r);
-    SV_REQUIRE(cs >= g, SV_ERR_SHAPE, "internal: LDS chunk too small");
-    a.chunk_sub = cs;
-    const int64_t tiles = (a.N + rows_tile - 1) / rows_tile;
-    SV_REQUIRE(tiles < (1ll << 31), SV_ERR_SHAPE, "too many rows");
-    a.n_tiles = static_cast<int>(tiles);
-    const int grid = static_cast<int>(std::min<int64_t>(tiles, grid_cap));
-    const size_t lds = static_cast<size_t>(M) * cs * kActRec + fixed;
-    KernelFn fn = pick_kernel(qt, gl, M);
-    SV_REQUIRE(fn, SV_ERR_ARG, "internal: no kernel for this M");
-    hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, st, a);
-    return hip_check(hipGetLastError(), "verify_matvec launch");
-}
-
-static void fill_act(MvArgs &a, const sv_act *A) {
-    a.K = A->K;
-    a.aq = A->q;
-    a.ad = A->d;
-    a.as16 = A->s16;
-    a.in_parts = A->sumsq_parts;
-    a.n_parts = A->sumsq_parts ? A->n_parts : 0;
-    a.eps = A->eps;
-}
-
-}  // namespace sv
-
-extern "C" int sv_verify_matvec(const sv_weight *W, int32_t n_w, const sv_act *A, float *const *y,
-                                const sv_epilogue *ep, void *stream) {
-    using namespace sv;
-    SV_REQUIRE(W, SV_ERR_ARG, "verify_matvec: W is NULL");
-    SV_REQUIRE(n_w >= 1 && n_w <= 3, SV_ERR_ARG, "verify_matvec: n_w must be 1..3");
+// Fill a PhaseDesc from ABI arguments (no scratch pointers yet).
+static int make_phase(PhaseDesc &P, const sv_weight *W, int32_t n_w, const sv_act *A, float *const *y,
+                      const sv_epilogue *ep, const int32_t *row_ids, int64_t n_rows, uint64_t *argmax) {
+    SV_REQUIRE(W, SV_ERR_ARG, "weights are NULL");
+    SV_REQUIRE(n_w >= 1 && n_w <= 3, SV_ERR_ARG, "n_w must be 1..3");
     int rc = validate_act(A);
     if (rc) return rc;
     for (int i = 0; i < n_w; i++) {
         rc = validate_weight(W[i], A->K);
         if (rc) return rc;
         SV_REQUIRE(W[i].qtype == W[0].qtype && W[i].rows == W[0].rows, SV_ERR_SHAPE,
-                   "verify_matvec: matrices sharing an input must have the same qtype and rows");
+                   "matrices sharing an input must have the same qtype and rows");
     }
-    MvArgs a{};
-    a.n_w = n_w;
-    a.N = W[0].rows;
-    a.wrows = W[0].rows;
+    P = PhaseDesc{};
+    P.qtype = W[0].qtype;
+    P.n_w = n_w;
+    P.wrows = static_cast<int32_t>(W[0].rows);
+    P.N = static_cast<int32_t>(row_ids ? n_rows : W[0].rows);
+    P.K = static_cast<int32_t>(A->K);
     Streams s;
     streams_of(W[0].qtype, W[0].rows, W[0].cols, &s);
-    a.o1 = s.off[1];
-    a.o2 = s.off[2];
-    a.o3 = s.off[3];
+    P.o1 = s.off[1];
+    P.o2 = s.off[2];
+    P.o3 = s.off[3];
     for (int i = 0; i < n_w; i++) {
-        a.w[i] = static_cast<const uint8_t *>(W[i].data);
-        a.y[i] = y ? y[i] : nullptr;
-        if (a.y[i]) SV_REQUIRE(aligned(a.y[i], 4), SV_ERR_ALIGN, "verify_matvec: y must be 4-byte aligned");
+        P.w[i] = static_cast<const uint8_t *>(W[i].data);
+        P.y[i] = y ? y[i] : nullptr;
+        if (P.y[i]) SV_REQUIRE(aligned(P.y[i], 4), SV_ERR_ALIGN, "outputs must be 4-byte aligned");
     }
-    fill_act(a, A);
-    a.ep_mode = SV_EP_NONE;
+    P.row_ids = row_ids;
+    P.aq = A->q;
+    P.ad = A->d;
+    P.as16 = A->s16;
+    P.in_parts = A->sumsq_parts;
+    P.n_parts = A->sumsq_parts ? A->n_parts : 0;
+    P.eps = A->eps;
+    P.argmax = reinterpret_cast<unsigned long long *>(argmax);
+    P.ep_mode = SV_EP_NONE;
     if (ep && ep->mode != SV_EP_NONE) {
-        SV_REQUIRE(ep->mode == SV_EP_QUANT || ep->mode == SV_EP_PAIR, SV_ERR_ARG, "verify_matvec: bad epilogue mode");
-        SV_REQUIRE(a.N % 32 == 0, SV_ERR_SHAPE, "verify_matvec: epilogue needs rows % 32 == 0");
-        SV_REQUIRE(ep->q && ep->d && ep->s16 && ep->sumsq, SV_ERR_ARG, "verify_matvec: epilogue outputs are NULL");
+        SV_REQUIRE(ep->mode == SV_EP_QUANT || ep->mode == SV_EP_PAIR, SV_ERR_ARG, "bad epilogue mode");
+        SV_REQUIRE(P.N % 32 == 0, SV_ERR_SHAPE, "the epilogue needs rows % 32 == 0");
+        SV_REQUIRE(ep->q && ep->d && ep->s16 && ep->sumsq, SV_ERR_ARG, "epilogue outputs are NULL");
         SV_REQUIRE(aligned(ep->q, 16) && aligned(ep->d, 4) && aligned(ep->s16, 8) && aligned(ep->sumsq, 4) &&
                        (!ep->gamma || aligned(ep->gamma, 4)),
-                   SV_ERR_ALIGN, "verify_matvec: epilogue buffer alignment");
+                   SV_ERR_ALIGN, "epilogue buffer alignment");
         if (ep->mode == SV_EP_QUANT)
-            SV_REQUIRE(ep->src >= 0 && ep->src < n_w, SV_ERR_ARG, "verify_matvec: epilogue src out of range");
+            SV_REQUIRE(ep->src >= 0 && ep->src < n_w, SV_ERR_ARG, "epilogue src out of range");
         else
-            SV_REQUIRE(n_w == 2, SV_ERR_ARG, "verify_matvec: pair epilogue needs exactly two matrices");
-        a.ep_mode = ep->mode;
-        a.ep_src = ep->src;
-        a.gamma = ep->gamma;
-        a.oq = ep->q;
-        a.od = ep->d;
-        a.os16 = ep->s16;
-        a.osumsq = ep->sumsq;
+            SV_REQUIRE(n_w == 2, SV_ERR_ARG, "the pair epilogue needs exactly two matrices");
+        P.ep_mode = ep->mode;
+        P.ep_src = ep->src;
+        P.gamma = ep->gamma;
+        P.oq = ep->q;
+        P.od = ep->d;
+        P.os16 = ep->s16;
+        P.osumsq = ep->sumsq;
     }
-    return launch(a, W[0].qtype, A->M, 1 << 30, as_stream(stream));
+    decompose(P);
+    return SV_OK;
+}
+
+// Scratch of a phase: a fixed counter region (the same for every call, so
+// a workspace shared by calls of different shapes never has partial sums
+// where another call keeps its counters) followed by the partial sums.
+constexpr size_t kCounterBytes = 256 * 1024;
+constexpr int kMaxTiles = static_cast<int>(kCounterBytes / 4);
+
+static size_t phase_scratch(const PhaseDesc &P, int M) {
+    if (!needs_partials(P)) return 0;
+    return kCounterBytes + partial_bytes(P, M);
+}
+
+static int launch_single(PhaseDesc &P, int M, void *ws, size_t ws_bytes, hipStream_t st) {
+    const size_t need = phase_scratch(P, M);
+    if (needs_partials(P)) {
+        SV_REQUIRE(ws && ws_bytes >= need, SV_ERR_WORKSPACE,
+                   "workspace needs " + std::to_string(need) + " bytes");
+        SV_REQUIRE(aligned(ws, 256), SV_ERR_ALIGN, "workspace must be 256-byte aligned");
+        SV_REQUIRE(P.n_tiles <= kMaxTiles, SV_ERR_SHAPE, "too many row tiles for the counter region");
+        uint8_t *b = static_cast<uint8_t *>(ws);
+        P.tile_count = reinterpret_cast<unsigned *>(b);
+        P.partial = reinterpret_cast<float *>(b + kCounterBytes);
+    }
+    const int CS = P.chunk_sub;
+    const size_t lds = lds_bytes(M, CS);
+    SV_REQUIRE(lds <= 64 * 1024, SV_ERR_SHAPE, "internal: LDS budget exceeded");
+    launch_any(M, false, P, nullptr, 0, nullptr, P.n_units, CS, lds, st);
+    return hip_check(hipGetLastError(), "projection launch");
+}
+
+}  // namespace sv
+
+// ----------------------------------------------------------------- ABI
+extern "C" size_t sv_matvec_workspace_bytes(const sv_weight *W, int32_t n_w, const sv_act *A) {
+    sv::PhaseDesc P;
+    if (sv::make_phase(P, W, n_w, A, nullptr, nullptr, nullptr, 0, nullptr) != SV_OK) return 0;
+    // sized for any epilogue: two matrices may be paired
+    if (n_w == 2) P.ep_mode = SV_EP_PAIR;
+    return sv::phase_scratch(P, A->M);
+}
+
+extern "C" int sv_verify_matvec(const sv_weight *W, int32_t n_w, const sv_act *A, float *const *y,
+                                const sv_epilogue *ep, void *workspace, size_t ws_bytes, void *stream) {
+    sv::PhaseDesc P;
+    int rc = sv::make_phase(P, W, n_w, A, y, ep, nullptr, 0, nullptr);
+    if (rc) return rc;
+    return sv::launch_single(P, A->M, workspace, ws_bytes, sv::as_stream(stream));
+}
+
+extern "C" size_t sv_head_workspace_bytes(const sv_weight *H, const sv_act *A, int64_t n_rows) {
+    sv::PhaseDesc P;
+    if (sv::make_phase(P, H, 1, A, nullptr, nullptr, nullptr, 0, nullptr) != SV_OK) return 0;
+    if (n_rows > 0) {
+        P.N = static_cast<int32_t>(n_rows);
+        sv::decompose(P);
+    }
+    return sv::phase_scratch(P, A->M);
 }
 
 extern "C" int sv_head_logits(const sv_weight *H, const sv_act *A, const int32_t *row_ids, int64_t n_rows,
-                              float *logits, uint64_t *argmax, void *stream) {
+                              float *logits, uint64_t *argmax, void *workspace, size_t ws_bytes, void *stream) {
     using namespace sv;
     SV_REQUIRE(H, SV_ERR_ARG, "head_logits: H is NULL");
-    int rc = validate_act(A);
-    if (rc) return rc;
-    rc = validate_weight(*H, A->K);
-    if (rc) return rc;
     if (!row_ids) n_rows = H->rows;
     SV_REQUIRE(n_rows >= 1 && n_rows < (1ll << 31), SV_ERR_SHAPE, "head_logits: n_rows out of range");
     SV_REQUIRE(logits || argmax, SV_ERR_ARG, "head_logits: nothing to write");
     SV_REQUIRE(!logits || aligned(logits, 4), SV_ERR_ALIGN, "head_logits: logits must be 4-byte aligned");
     SV_REQUIRE(!argmax || aligned(argmax, 8), SV_ERR_ALIGN, "head_logits: argmax must be 8-byte aligned");
     SV_REQUIRE(!row_ids || aligned(row_ids, 4), SV_ERR_ALIGN, "head_logits: row_ids must be 4-byte aligned");
-    MvArgs a{};
-    a.n_w = 1;
-    a.N = n_rows;
-    a.wrows = H->rows;
-    Streams s;
-    streams_of(H->qtype, H->rows, H->cols, &s);
-    a.o1 = s.off[1];
-    a.o2 = s.off[2];
-    a.o3 = s.off[3];
-    a.w[0] = static_cast<const uint8_t *>(H->data);
-    a.y[0] = logits;
-    a.row_ids = row_ids;
-    a.argmax = reinterpret_cast<unsigned long long *>(argmax);
-    fill_act(a, A);
-    a.ep_mode = SV_EP_NONE;
+    float *ys[1] = {logits};
+    PhaseDesc P;
+    int rc = make_phase(P, H, 1, A, ys, nullptr, row_ids, n_rows, argmax);
+    if (rc) return rc;
     hipStream_t st = as_stream(stream);
     if (argmax) {
-        hipLaunchKernelGGL(zero_u64, dim3(1), dim3(64), 0, st, a.argmax, A->M);
+        hipLaunchKernelGGL(zero_u64, dim3(1), dim3(64), 0, st, P.argmax, A->M);
         rc = hip_check(hipGetLastError(), "head_logits init");
         if (rc) return rc;
     }
-    return launch(a, H->qtype, A->M, 1024, st);
+    return launch_single(P, A->M, workspace, ws_bytes, st);
 }
+
+// ------------------------------------------------------------ whole pass
+struct sv_pass {
+    int M, n_phases, grid, CS;
+    uint32_t n_tickets;
+    sv::PhaseDesc *table;        // device
+    unsigned *ctl;               // device: status, exit count, completion slots
+    unsigned long long *argmax;  // device (or null): zeroed per run
+    unsigned long long *trace;   // device: [kMaxGrid][n_phases][4] timestamps
+    bool tracing;
+    std::vector<sv::PhaseDesc> host;
+};
+
+extern "C" size_t sv_pass_workspace_bytes(const sv_phase *phases, int32_t n_phases) {
+    size_t need = 0;
+    if (!phases || n_phases < 1) return 0;
+    size_t max_scratch = 0;
+    int M = 0;
+    for (int i = 0; i < n_phases; i++) {
+        sv::PhaseDesc P;
+        const sv_phase &ph = phases[i];
+        if (sv::make_phase(P, ph.W, ph.n_w, &ph.A, ph.y, ph.ep.mode ? &ph.ep : nullptr, ph.row_ids, ph.n_rows,
+                           ph.argmax) != SV_OK)
+            return 0;
+        M = ph.A.M;
+        max_scratch = std::max(max_scratch, sv::phase_scratch(P, M));
+    }
+    need += (static_cast<size_t>(n_phases) * sizeof(sv::PhaseDesc) + 255) / 256 * 256;
+    need += (static_cast<size_t>(sv::kSlotStride) * (1 + n_phases * sv::kSlots) * 4 + 255) / 256 * 256;
+    need += (static_cast<size_t>(sv::kMaxGrid) * n_phases * 32 + 255) / 256 * 256;
+    need += max_scratch;
+    return need;
+}
+
+extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *workspace, size_t ws_bytes,
+                              sv_pass **out) {
+    using namespace sv;
+    SV_REQUIRE(out, SV_ERR_ARG, "pass_create: out is NULL");
+    *out = nullptr;
+    SV_REQUIRE(phases && n_phases >= 1, SV_ERR_ARG, "pass_create: no phases");
+    const size_t need = sv_pass_workspace_bytes(phases, n_phases);
+    SV_REQUIRE(need > 0, SV_ERR_ARG, "pass_create: invalid phase (" + std::string(sv_last_error()) + ")");
+    SV_REQUIRE(workspace && ws_bytes >= need, SV_ERR_WORKSPACE,
+               "pass_create: workspace needs " + std::to_string(need) + " bytes");
+    SV_REQUIRE(aligned(workspace, 256), SV_ERR_ALIGN, "pass_create: workspace must be 256-byte aligned");
+    sv_pass *p = new sv_pass();
+    p->n_phases = n_phases;
+    p->host.resize(n_phases);
+    uint8_t *b = static_cast<uint8_t *>(workspace);
+    const size_t table_bytes = (static_cast<size_t>(n_phases) * sizeof(PhaseDesc) + 255) / 256 * 256;
+    const size_t ctl_bytes = (static_cast<size_t>(kSlotStride) * (1 + n_phases * kSlots) * 4 + 255) / 256 * 256;
+    p->table = reinterpret_cast<PhaseDesc *>(b);
+    p->ctl = reinterpret_cast<unsigned *>(b + table_bytes);
+    const size_t trace_bytes = (static_cast<size_t>(kMaxGrid) * n_phases * 32 + 255) / 256 * 256;
+    p->trace = reinterpret_cast<unsigned long long *>(b + table_bytes + ctl_bytes);
+    p->tracing = false;
+    uint8_t *scratch = b + table_bytes + ctl_bytes + trace_bytes;
+    uint32_t tickets = 0;
+    for (int i = 0; i < n_phases; i++) {
+        PhaseDesc &P = p->host[i];
+        const sv_phase &ph = phases[i];
+        make_phase(P, ph.W, ph.n_w, &ph.A, ph.y, ph.ep.mode ? &ph.ep : nullptr, ph.row_ids, ph.n_rows,
+                   ph.argmax);
+        if (i == 0) p->M = ph.A.M;
+        if (ph.A.M != p->M) {
+            delete p;
+            return fail(SV_ERR_SHAPE, "pass_create: all phases need the same M");
+        }
+        if (P.n_tiles > kMaxTiles) {
+            delete p;
+            return fail(SV_ERR_SHAPE, "pass_create: too many row tiles for the counter region");
+        }
+        P.tile_count = reinterpret_cast<unsigned *>(scratch);
+        P.partial = reinterpret_cast<float *>(scratch + kCounterBytes);
+        P.ready = p->ctl + kSlotStride * (1 + i * kSlots);
+        P.wait = (i > 0) ? p->ctl + kSlotStride * (1 + (i - 1) * kSlots) : nullptr;
+        P.wait_target = (i > 0) ? static_cast<uint32_t>(p->host[i - 1].n_units) : 0u;
+        P.unit_base = tickets;
+        tickets += static_cast<uint32_t>(P.n_units);
+        if (P.argmax) p->argmax = P.argmax;
+    }
+    p->n_tickets = tickets;
+    // Each phase's requantised output must have addresses of its own within
+    // the pass: consumers read it through their L2, which can hold no stale
+    // copy of an address written only once per launch.
+    {
+        std::vector<std::pair<uintptr_t, uintptr_t>> spans;
+        for (auto &P : p->host) {
+            if (P.ep_mode == SV_EP_NONE) continue;
+            const uintptr_t M = static_cast<uintptr_t>(p->M), N = static_cast<uintptr_t>(P.N);
+            const std::pair<const void *, uintptr_t> outs[4] = {
+                {P.oq, M * N}, {P.od, M * N / 8}, {P.os16, M * N / 4}, {P.osumsq, M * N / 8}};
+            for (auto &o : outs) {
+                const uintptr_t a = reinterpret_cast<uintptr_t>(o.first) & ~static_cast<uintptr_t>(255);
+                const uintptr_t b = (reinterpret_cast<uintptr_t>(o.first) + o.second + 255) & ~static_cast<uintptr_t>(255);
+                spans.push_back({a, b});
+            }
+        }
+        std::sort(spans.begin(), spans.end());
+        for (size_t i = 1; i < spans.size(); i++)
+            if (spans[i].first < spans[i - 1].second) {
+                delete p;
+                return fail(SV_ERR_ARG, "pass_create: the requantised outputs of different phases share "
+                                        "256-byte blocks; every phase needs buffers of its own");
+            }
+    }
+    int chunk = 0;
+    for (auto &P : p->host) chunk = std::max(chunk, P.chunk_sub);
+    p->CS = chunk;
+    int dev = 0;
+    hipDeviceProp_t prop;
+    int rc = hip_check(hipGetDevice(&dev), "pass_create");
+    if (!rc) rc = hip_check(hipGetDeviceProperties(&prop, dev), "pass_create");
+    if (rc) {
+        delete p;
+        return rc;
+    }
+    // Every workgroup of the pass must be resident at once (they wait on each
+    // other's phases): the grid is what the GPU holds of this kernel.
+    const int occ = occupancy_any(p->M, lds_bytes(p->M, p->CS));
+    if (occ < 1) {
+        delete p;
+        return fail(SV_ERR_HIP, "pass_create: could not query occupancy");
+    }
+    p->grid = std::min(prop.multiProcessorCount * std::min(occ, 2), kMaxGrid);
+    rc = hip_check(hipMemcpy(p->table, p->host.data(), static_cast<size_t>(n_phases) * sizeof(PhaseDesc),
+                             hipMemcpyHostToDevice),
+                   "pass_create upload");
+    if (!rc) rc = hip_check(hipMemset(p->ctl, 0, ctl_bytes), "pass_create ctl");
+    if (!rc) rc = hip_check(hipMemset(p->trace, 0, trace_bytes), "pass_create trace");
+    if (!rc) rc = hip_check(hipMemset(scratch, 0, ws_bytes - table_bytes - ctl_bytes - trace_bytes),
+                            "pass_create scratch");
+    if (rc) {
+        delete p;
+        return rc;
+    }
+    *out = p;
+    return SV_OK;
+}
+
+extern "C" int sv_pass_run(const sv_pass *p, void *stream) {
+    using namespace sv;
+    SV_REQUIRE(p, SV_ERR_ARG, "pass_run: NULL pass");
+    hipStream_t st = as_stream(stream);
+    const size_t lds = lds_bytes(p->M, p->CS);
+    SV_REQUIRE(lds <= 64 * 1024, SV_ERR_SHAPE, "internal: LDS budget exceeded");
+    launch_any(p->M, true, PhaseDesc{}, p->table, p->n_phases, p->ctl, p->grid, p->CS, lds, st, p->argmax,
+               p->tracing ? p->trace : nullptr);
+    return hip_check(hipGetLastError(), "pass_run launch");
+}
+
+extern "C" int sv_pass_status(const sv_pass *p, uint32_t *status) {
+    SV_REQUIRE(p && status, SV_ERR_ARG, "pass_status: NULL argument");
+    return sv::hip_check(hipMemcpy(status, p->ctl + 1, 4, hipMemcpyDeviceToHost), "pass_status");
+}
+
+extern "C" int sv_pass_trace(sv_pass *p, int enable, uint64_t *host, size_t bytes, int32_t *grid) {
+    using namespace sv;
+    SV_REQUIRE(p, SV_ERR_ARG, "pass_trace: NULL pass");
+    p->tracing = enable != 0;
+    if (grid) *grid = p->grid;
+    if (!host) return SV_OK;
+    const size_t need = static_cast<size_t>(p->grid) * p->n_phases * 32;
+    SV_REQUIRE(bytes >= need, SV_ERR_WORKSPACE, "pass_trace: host buffer needs " + std::to_string(need) + " bytes");
+    return hip_check(hipMemcpy(host, p->trace, need, hipMemcpyDeviceToHost), "pass_trace");
+}
+
+extern "C" void sv_pass_destroy(sv_pass *p) { delete p; }

@@ -94,7 +94,8 @@ def _mv(ws, A, ep=None):
     n = len(ws)
     W = (sv.Weight * n)(*ws)
     Y = (ctypes.c_void_p * n)(*([FAKE.value] * n))
-    return sv.lib().sv_verify_matvec(W, n, ctypes.byref(A), Y, None if ep is None else ctypes.byref(ep), None)
+    return sv.lib().sv_verify_matvec(W, n, ctypes.byref(A), Y, None if ep is None else ctypes.byref(ep), None, 0,
+                                     None)
 
 
 def test_matvec_rejects():
@@ -108,7 +109,7 @@ def test_matvec_rejects():
     _err(_mv([_w(), _w(rows=32)], _act()), sv.SV_ERR_SHAPE)     # rows differ
     _err(_mv([_w(), _w(qt=14)], _act()), sv.SV_ERR_SHAPE)       # qtypes differ
     W = (sv.Weight * 4)(*([_w()] * 4))
-    rc = sv.lib().sv_verify_matvec(W, 4, ctypes.byref(_act()), None, None, None)
+    rc = sv.lib().sv_verify_matvec(W, 4, ctypes.byref(_act()), None, None, None, 0, None)
     _err(rc, sv.SV_ERR_ARG)
     ep = sv.Epilogue(7, 0, None, FAKE.value, FAKE.value, FAKE.value, FAKE.value)
     _err(_mv([_w()], _act(), ep), sv.SV_ERR_ARG)
@@ -123,8 +124,17 @@ def test_matvec_rejects():
 def test_head_and_accept_rejects():
     L = sv.lib()
     H = _w(qt=14)
-    _err(L.sv_head_logits(ctypes.byref(H), ctypes.byref(_act()), None, 0, None, None, None), sv.SV_ERR_ARG)
-    _err(L.sv_head_logits(ctypes.byref(H), ctypes.byref(_act()), FAKE, 0, FAKE, None, None), sv.SV_ERR_SHAPE)
+    _err(L.sv_head_logits(ctypes.byref(H), ctypes.byref(_act()), None, 0, None, None, None, 0, None),
+         sv.SV_ERR_ARG)
+    _err(L.sv_head_logits(ctypes.byref(H), ctypes.byref(_act()), FAKE, 0, FAKE, None, None, 0, None),
+         sv.SV_ERR_SHAPE)
+    # a split head needs a workspace
+    H2 = _w(qt=14, rows=4096, cols=5120)
+    A2 = _act(K=5120)
+    need = L.sv_head_workspace_bytes(ctypes.byref(H2), ctypes.byref(A2), 0)
+    assert need > 0
+    _err(L.sv_head_logits(ctypes.byref(H2), ctypes.byref(A2), None, 0, FAKE, None, None, 0, None),
+         sv.SV_ERR_WORKSPACE)
     _err(L.sv_accept_greedy(FAKE, None, FAKE, 16, FAKE, None), sv.SV_ERR_ARG)
     _err(L.sv_accept_greedy(FAKE_ODD, None, FAKE, 4, FAKE, None), sv.SV_ERR_ALIGN)
     ws = sv.accept_workspace_bytes(151936, 4)
@@ -136,6 +146,39 @@ def test_head_and_accept_rejects():
          sv.SV_ERR_WORKSPACE)
     _err(L.sv_accept_rejection(FAKE, 0, None, FAKE, 4, FAKE, ctypes.c_float(1.0), FAKE, ws, FAKE, None),
          sv.SV_ERR_SHAPE)
+
+
+def test_workspace_sizes():
+    """K is cut into ceil(steps / 12) chunks of 256-element steps; partial sums
+    (after a fixed 256 KiB counter region) are needed when K is split or two
+    matrices may be paired, and nothing otherwise."""
+    L = sv.lib()
+    for rows, cols, qt, n_w, M, S in [(2560, 2560, 12, 3, 5, 1), (2560, 9728, 14, 1, 5, 4), (9728, 2560, 12, 2, 16, 1),
+                                      (5120, 17408, 14, 1, 5, 6), (17408, 5120, 12, 1, 8, 2)]:
+        steps = -(-cols // 256)
+        assert -(-steps // 12) == S
+        W = (sv.Weight * n_w)(*([_w(qt=qt, rows=rows, cols=cols)] * n_w))
+        need = L.sv_matvec_workspace_bytes(W, n_w, ctypes.byref(_act(M=M, K=cols)))
+        if S == 1 and n_w != 2:
+            assert need == 0
+        else:
+            assert need == 256 * 1024 + n_w * S * M * rows * 4
+
+
+def test_pass_rejects():
+    L = sv.lib()
+    W1 = (sv.Weight * 1)(_w(qt=12, rows=64, cols=256))
+    W2 = (sv.Weight * 1)(_w(qt=12, rows=64, cols=512))
+    a1, a2 = _act(K=256), _act(M=3, K=512)
+    ph = (sv.Phase * 2)()
+    ph[0].W, ph[0].n_w, ph[0].A = ctypes.cast(W1, ctypes.POINTER(sv.Weight)), 1, a1
+    ph[1].W, ph[1].n_w, ph[1].A = ctypes.cast(W2, ctypes.POINTER(sv.Weight)), 1, a2
+    assert L.sv_pass_workspace_bytes(ph, 2) > 0
+    h = ctypes.c_void_p()
+    # M differs between phases
+    _err(L.sv_pass_create(ph, 2, FAKE, 1 << 30, ctypes.byref(h)), sv.SV_ERR_SHAPE)
+    _err(L.sv_pass_create(ph, 2, FAKE, 16, ctypes.byref(h)), sv.SV_ERR_WORKSPACE)
+    _err(L.sv_pass_create(ph, 0, FAKE, 1 << 30, ctypes.byref(h)), sv.SV_ERR_ARG)
 
 
 def test_argmax_index_decode():

@@ -125,7 +125,7 @@ def _encode_unit(qt, w):
 
 
 # ------------------------------------------------------------------ a3 tolerance parity
-SHAPES = [(96, 1024), (64, 2560), (160, 5120), (32, 768)]
+SHAPES = [(96, 1024), (64, 2560), (160, 5120), (32, 768), (64, 9728), (32, 17408)]
 
 
 @pytest.mark.parametrize("qt", QT)
