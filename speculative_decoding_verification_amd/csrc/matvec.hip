@@ -55,6 +55,7 @@ struct PhaseDesc {
     int32_t qtype, n_w;
     int32_t N, K, wrows;
     int32_t S, steps, n_tiles, per_tile, n_units, chunk_sub;
+    int32_t count_all;        // 0: only units of matrix ep_src feed the next phase
     uint64_t o1, o2, o3;
     const int32_t *row_ids;
     const int8_t *aq;
@@ -98,34 +99,22 @@ struct WRaw<SV_Q6_K> {
     uint32_t sc, d;
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint4 ld_stream16(const uint8_t *p) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint2 ld_stream8(const uint8_t *p) {
-    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
-    return make_uint2(v.x, v.y);
-}
-
 template <int QT>
 __device__ __forceinline__ void load_w(WRaw<QT> &r, const uint8_t *__restrict__ w, const PhaseDesc &P, int64_t row,
                                        int64_t s) {
     const int64_t K = P.K, nsub = K >> 5;
     if constexpr (QT == SV_Q8_0) {
-        r.q0 = ld_stream16(w + row * K + s * 32);
-        r.q1 = ld_stream16(w + row * K + s * 32 + 16);
-        r.d = *reinterpret_cast<const uint16_t *>(w + P.o1 + (row * nsub + s) * 2);
+        r.q0 = gld16_nt(w + row * K + s * 32);
+        r.q1 = gld16_nt(w + row * K + s * 32 + 16);
+        r.d = gld(reinterpret_cast<const uint16_t *>(w + P.o1 + (row * nsub + s) * 2));
     } else if constexpr (QT == SV_Q4_K) {
-        r.q = ld_stream16(w + (row * nsub + s) * 16);
-        r.h = *reinterpret_cast<const uint4 *>(w + P.o1 + (row * (K >> 8) + (s >> 3)) * 16);
+        r.q = gld16_nt(w + (row * nsub + s) * 16);
+        r.h = gld16(w + P.o1 + (row * (K >> 8) + (s >> 3)) * 16);
     } else {
-        r.l = ld_stream16(w + (row * nsub + s) * 16);
-        r.h = ld_stream8(w + P.o1 + (row * nsub + s) * 8);
-        r.sc = *reinterpret_cast<const uint16_t *>(w + P.o2 + row * (K >> 4) + 2 * s);
-        r.d = *reinterpret_cast<const uint16_t *>(w + P.o3 + (row * (K >> 8) + (s >> 3)) * 2);
+        r.l = gld16_nt(w + (row * nsub + s) * 16);
+        r.h = gld8_nt(w + P.o1 + (row * nsub + s) * 8);
+        r.sc = gld(reinterpret_cast<const uint16_t *>(w + P.o2 + row * (K >> 4) + 2 * s));
+        r.d = gld(reinterpret_cast<const uint16_t *>(w + P.o3 + (row * (K >> 8) + (s >> 3)) * 2));
     }
 }
 
@@ -243,25 +232,8 @@ struct Shared {
     unsigned long long best[SV_MAX_M];
     int last;
     unsigned abort;
-    unsigned long long t_wait;
+    unsigned long long t_wait, t_staged, t_computed;   // first unit of a phase (trace)
 };
-
-// Cross-workgroup data of one launch (partial sums, the next phase's
-// activation, counters) moves through device-coherent accesses (sc1: written
-// through to, and read from, the level all XCDs share) instead of fences:
-// an agent-scope fence writes back or invalidates a whole L2, which is far
-// too costly once per unit.  Ordering comes from s_waitcnt before the
-// barrier that precedes each counter update.
-template <typename T>
-__device__ __forceinline__ void st_dev(T *p, T v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_dev(const T *p) {
-    return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until this wave's memory operations have completed.
-__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Completion of a phase is counted in kSlots counters kSlotStride words
 // apart (unit u adds to slot u % kSlots), so finishing units do not all
@@ -269,7 +241,7 @@ __device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
 constexpr int kSlots = 8;
 constexpr int kSlotStride = 64;
 
-__device__ bool wait_ready(const unsigned *ctr, unsigned target, unsigned *status, unsigned &abort_sh) {
+__device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target, unsigned *status, unsigned &abort_sh) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         unsigned n = 0;
@@ -280,14 +252,14 @@ __device__ bool wait_ready(const unsigned *ctr, unsigned target, unsigned *statu
             for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
             v = __shfl(v, 0, 64);
             if (v >= target) break;
-            if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || ++n > kSpinLimit) {
+            if (ld_dev(status) != 0u || ++n > kSpinLimit) {
                 ok = false;
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
         }
         if (lane == 0) {
-            if (!ok) atomicOr(status, 1u);
+            if (!ok) or_dev(status, 1u);
             abort_sh = ok ? 0u : 1u;
         }
     }
@@ -304,7 +276,7 @@ constexpr int kStageHalf = 6;   // >= 8 positions * 96 sub-blocks * 2 halves / 2
 constexpr int kStageRec = 3;    // >= 8 * 96 / 256
 constexpr int kPartsPerLane = 9;  // >= 544 partials / 64 lanes
 
-__device__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int64_t s0, int cs, int CS,
+__device__ __forceinline__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int64_t s0, int cs, int CS,
                           float *rs, int M) {
     const int64_t K = P.K, nsub = K >> 5;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -318,57 +290,66 @@ __device__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int6
 #pragma unroll
             for (int j = 0; j < kPartsPerLane; j++) {
                 const int i = lane + 64 * j;
-                pv[k][j] = (m < M && i < P.n_parts) ? P.in_parts[m * P.n_parts + i] : 0.0f;
+                pv[k][j] = (m < M && i < P.n_parts) ? gld(P.in_parts + m * P.n_parts + i) : 0.0f;
             }
         }
     }
     const int nhalf = mg * cs * 2, nrec = mg * cs;
-    uint4 hv[kStageHalf];
-    float dv[kStageRec];
-    int2 sv[kStageRec];
-#pragma unroll
-    for (int k = 0; k < kStageHalf; k++) {
-        const int i = threadIdx.x + k * kThreads;
-        if (i < nhalf) {
-            const int m = i / (cs * 2), r = i % (cs * 2), sl = r >> 1, h = r & 1;
-            hv[k] = *reinterpret_cast<const uint4 *>(P.aq + (m0 + m) * K + (s0 + sl) * 32 + h * 16);
-        }
+    // named registers, not arrays: a private array here ends up in scratch
+    uint4 h0, h1, h2, h3, h4, h5;
+#define SV_LDH(k, hv)                                                                                   \
+    {                                                                                                   \
+        const int i = threadIdx.x + (k) * kThreads;                                                     \
+        if (i < nhalf) {                                                                                \
+            const int m = i / (cs * 2), r = i % (cs * 2), sl = r >> 1, h = r & 1;                        \
+            hv = gld16(P.aq + (m0 + m) * K + (s0 + sl) * 32 + h * 16);                                    \
+        }                                                                                               \
     }
-#pragma unroll
-    for (int k = 0; k < kStageRec; k++) {
-        const int i = threadIdx.x + k * kThreads;
-        if (i < nrec) {
-            const int m = i / cs, sl = i % cs;
-            dv[k] = P.ad[(m0 + m) * nsub + s0 + sl];
-            sv[k] = *reinterpret_cast<const int2 *>(P.as16 + (m0 + m) * (K >> 4) + 2 * (s0 + sl));
-        }
+    SV_LDH(0, h0) SV_LDH(1, h1) SV_LDH(2, h2) SV_LDH(3, h3) SV_LDH(4, h4) SV_LDH(5, h5)
+#undef SV_LDH
+    float d0, d1, d2;
+    uint2 x0, x1, x2;
+#define SV_LDR(k, dv, xv)                                                                               \
+    {                                                                                                   \
+        const int i = threadIdx.x + (k) * kThreads;                                                     \
+        if (i < nrec) {                                                                                 \
+            const int m = i / cs, sl = i % cs;                                                          \
+            dv = gld(P.ad + (m0 + m) * nsub + s0 + sl);                                                 \
+            xv = gld8(P.as16 + (m0 + m) * (K >> 4) + 2 * (s0 + sl));                                    \
+        }                                                                                               \
     }
-#pragma unroll
-    for (int k = 0; k < kStageHalf; k++) {
-        const int i = threadIdx.x + k * kThreads;
-        if (i < nhalf) {
-            const int m = i / (cs * 2), r = i % (cs * 2), sl = r >> 1, h = r & 1;
-            *reinterpret_cast<uint4 *>(act + m * CS * kActRec + h * CS * 16 + sl * 16) = hv[k];
-        }
+    SV_LDR(0, d0, x0) SV_LDR(1, d1, x1) SV_LDR(2, d2, x2)
+#undef SV_LDR
+#define SV_STH(k, hv)                                                                                   \
+    {                                                                                                   \
+        const int i = threadIdx.x + (k) * kThreads;                                                     \
+        if (i < nhalf) {                                                                                \
+            const int m = i / (cs * 2), r = i % (cs * 2), sl = r >> 1, h = r & 1;                        \
+            *reinterpret_cast<uint4 *>(act + m * CS * kActRec + h * CS * 16 + sl * 16) = hv;              \
+        }                                                                                               \
     }
-#pragma unroll
-    for (int k = 0; k < kStageRec; k++) {
-        const int i = threadIdx.x + k * kThreads;
-        if (i < nrec) {
-            const int m = i / cs, sl = i % cs;
-            uint8_t *am = act + m * CS * kActRec;
-            reinterpret_cast<float *>(am + CS * 32)[sl] = dv[k];
-            int2 x;
-            if (P.qtype == SV_Q4_K) {
-                x.x = __float_as_int(static_cast<float>(sv[k].x + sv[k].y));
-                x.y = 0;
-            } else {
-                x.x = -32 * sv[k].x;
-                x.y = -32 * sv[k].y;
-            }
-            reinterpret_cast<int2 *>(am + CS * 36)[sl] = x;
-        }
+    SV_STH(0, h0) SV_STH(1, h1) SV_STH(2, h2) SV_STH(3, h3) SV_STH(4, h4) SV_STH(5, h5)
+#undef SV_STH
+#define SV_STR(k, dv, xv)                                                                               \
+    {                                                                                                   \
+        const int i = threadIdx.x + (k) * kThreads;                                                     \
+        if (i < nrec) {                                                                                 \
+            const int m = i / cs, sl = i % cs;                                                          \
+            uint8_t *am = act + m * CS * kActRec;                                                       \
+            reinterpret_cast<float *>(am + CS * 32)[sl] = dv;                                           \
+            int2 x;                                                                                     \
+            if (P.qtype == SV_Q4_K) {                                                                   \
+                x.x = __float_as_int(static_cast<float>(static_cast<int32_t>(xv.x + xv.y)));            \
+                x.y = 0;                                                                                \
+            } else {                                                                                    \
+                x.x = -32 * static_cast<int32_t>(xv.x);                                                 \
+                x.y = -32 * static_cast<int32_t>(xv.y);                                                 \
+            }                                                                                           \
+            reinterpret_cast<int2 *>(am + CS * 36)[sl] = x;                                             \
+        }                                                                                               \
     }
+    SV_STR(0, d0, x0) SV_STR(1, d1, x1) SV_STR(2, d2, x2)
+#undef SV_STR
     if (rs) {
 #pragma unroll
         for (int k = 0; k < 4; k++) {
@@ -381,7 +362,7 @@ __device__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int6
 #pragma unroll
                     for (int j = 0; j < kPartsPerLane; j++) {
                         const int i = lane + 64 * j;
-                        pv[kk][j] = (mm < M && i < P.n_parts) ? P.in_parts[mm * P.n_parts + i] : 0.0f;
+                        pv[kk][j] = (mm < M && i < P.n_parts) ? gld(P.in_parts + mm * P.n_parts + i) : 0.0f;
                     }
                 }
             }
@@ -405,15 +386,15 @@ __device__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int6
 // of the matrices in [mat_lo, mat_hi), argmax candidates and the requantised
 // next activation.
 template <int M>
-__device__ void finish_tile(const PhaseDesc &P, const float *ystage, int64_t row0, int mat_lo, int mat_hi,
-                            bool do_ep, Shared<M> &sh) {
+__device__ __forceinline__ void finish_tile(const PhaseDesc &P, const float *ystage, int64_t row0, int mat_lo, int mat_hi,
+                            bool do_ep, float g_row, Shared<M> &sh) {
     const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), static_cast<int64_t>(P.N) - row0));
     for (int mat = mat_lo; mat < mat_hi; mat++) {
         float *y = P.y[mat];
         if (!y) continue;
         for (int i = threadIdx.x; i < M * kRows; i += kThreads) {
             const int m = i / kRows, r = i % kRows;
-            if (r < rows_here) y[static_cast<int64_t>(m) * P.N + row0 + r] = ystage[(mat * M + m) * kRows + r];
+            if (r < rows_here) gst(y + static_cast<int64_t>(m) * P.N + row0 + r, ystage[(mat * M + m) * kRows + r]);
         }
     }
     if (P.argmax) {
@@ -435,7 +416,7 @@ __device__ void finish_tile(const PhaseDesc &P, const float *ystage, int64_t row
             if (P.ep_mode == SV_EP_PAIR) v = ystage[(0 * M + m) * kRows + l32] * ystage[(1 * M + m) * kRows + l32];
             else v = ystage[(P.ep_src * M + m) * kRows + l32];
             const int64_t grow = row0 + l32;
-            const float vg = P.gamma ? v * P.gamma[grow] : v;
+            const float vg = P.gamma ? v * g_row : v;
             float am = fabsf(vg);
 #pragma unroll
             for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
@@ -473,7 +454,7 @@ struct MG {
 // sub-blocks per row, one 256-element super-block of a K-quant); lane j of
 // row group grp reads sub-block 8 t + j of rows row0 + 4 grp + p, p < 4.
 template <int QT, int M>
-__device__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart, int CS,
+__device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart, int CS,
                          Shared<M> &sh, bool do_wait, unsigned *status) {
     constexpr int MGV = MG<M>::value;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -498,7 +479,7 @@ __device__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ysta
     for (int p = 0; p < kR; p++) {
         int64_t rr = row0 + grp * kR + p;
         if (rr >= P.N) rr = 0;
-        const int64_t sr = P.row_ids ? static_cast<int64_t>(P.row_ids[rr]) : rr;
+        const int64_t sr = P.row_ids ? static_cast<int64_t>(gld(P.row_ids + rr)) : rr;
         // out-of-range ids are a caller error; clamp so no read leaves the matrix
         srow[p] = (sr < 0 || sr >= P.wrows) ? 0 : sr;
     }
@@ -513,6 +494,13 @@ __device__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ysta
 #pragma unroll
             for (int p = 0; p < kR; p++) load_w<QT>(raw[t][p], w, P, srow[p], sb);
         }
+    }
+    // the epilogue's norm weight of this thread's row, fetched off the
+    // critical path
+    float g_row = 1.0f;
+    if (P.gamma && P.ep_mode != SV_EP_NONE) {
+        const int64_t gr = row0 + (threadIdx.x & 31);
+        if (gr < P.N) g_row = gld(P.gamma + gr);
     }
     bool need_rs = false;
     if (do_wait) {
@@ -531,6 +519,7 @@ __device__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ysta
         __syncthreads();
         stage_act(act, P, m0, mg, s_begin, cs, CS, (need_rs && m0 == 0) ? sh.rscale : nullptr, M);
         __syncthreads();
+        if (do_wait && m0 == 0 && threadIdx.x == 0) sh.t_staged = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
         for (int t = 0; t < kMaxWaveSteps; t++) {
             const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
@@ -551,6 +540,7 @@ __device__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ysta
             }
         }
     }
+    if (do_wait && threadIdx.x == 0) sh.t_computed = __builtin_amdgcn_s_memrealtime();
     // Lanes of a row group: butterfly; waves: partials through LDS, added in
     // wave order.
 #pragma unroll
@@ -581,7 +571,7 @@ __device__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ysta
     }
     if (!split) {
         __syncthreads();
-        finish_tile<M>(P, ystage, row0, mat, mat + 1, mat == P.ep_src, sh);
+        finish_tile<M>(P, ystage, row0, mat, mat + 1, mat == P.ep_src, g_row, sh);
         return true;
     }
     // K split over units: the last unit of the tile to finish adds the chunk
@@ -589,8 +579,7 @@ __device__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ysta
     drain();
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(P.tile_count + tile, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = add_dev(P.tile_count + tile, 1u);
         sh.last = (prev == static_cast<unsigned>(per_tile - 1)) ? 1 : 0;
     }
     __syncthreads();
@@ -611,9 +600,9 @@ __device__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ysta
         ystage[(mt * M + m) * kRows + r] = s * sh.rscale[m];
     }
     if (threadIdx.x == 0)
-        __hip_atomic_store(P.tile_count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_dev(P.tile_count + tile, 0u);
     __syncthreads();
-    finish_tile<M>(P, ystage, row0, 0, P.n_w, true, sh);
+    finish_tile<M>(P, ystage, row0, 0, P.n_w, true, g_row, sh);
     return true;
 }
 
@@ -628,7 +617,7 @@ __device__ __forceinline__ bool dispatch_unit(const PhaseDesc &P, int unit, uint
 __device__ __forceinline__ void flush_best(const PhaseDesc &P, unsigned long long *best, int M) {
     __syncthreads();
     if (P.argmax && static_cast<int>(threadIdx.x) < M) {
-        if (best[threadIdx.x]) atomicMax(P.argmax + threadIdx.x, best[threadIdx.x]);
+        if (best[threadIdx.x]) max_dev(P.argmax + threadIdx.x, best[threadIdx.x]);
         best[threadIdx.x] = 0ull;
     }
     __syncthreads();
@@ -653,6 +642,11 @@ __global__ __launch_bounds__(kThreads) void phase_kernel(PhaseDesc P, int CS) {
     dispatch_unit<M>(P, blockIdx.x, smem, ystage, wpart, CS, sh, true, nullptr);
     flush_best(P, sh.best, M);
 }
+
+// Trace record of a (workgroup, phase): real-time counter at phase entry,
+// input ready, input staged, first unit computed, first unit done, last
+// unit done; units run; unused.
+constexpr int kTraceWords = 8;
 
 // ctl: [1] status, [2] exited workgroups, then per phase kSlots counters of
 // finished units.  The last workgroup to exit returns every counter but the
@@ -685,39 +679,45 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(const PhaseDesc *__restr
         __syncthreads();
         cur = p;
         bool first = true;
-        unsigned long long *tr = trace ? trace + (static_cast<size_t>(b) * n_phases + p) * 4 : nullptr;
+        unsigned long long *tr = trace ? trace + (static_cast<size_t>(b) * n_phases + p) * kTraceWords : nullptr;
         if (tr && threadIdx.x == 0) tr[0] = __builtin_amdgcn_s_memrealtime();
         unsigned n_done = 0;
         for (; u < nu; u += G) {
             ok = dispatch_unit<M>(P, static_cast<int>(u), smem, ystage, wpart, CS, sh, first, status);
             if (!ok) break;
-            if (first && tr && threadIdx.x == 0) tr[1] = sh.t_wait;
-            first = false;
             n_done++;
-            drain();
+            // Only units whose outputs the next phase reads are handed off
+            // (drained and counted); the last phase has no reader at all.
+            const bool counted = P.ready && (P.count_all || static_cast<int>((u % P.per_tile) / P.S) == P.ep_src);
+            if (counted) drain();
             __syncthreads();
             if (threadIdx.x == 0) {
-                if (P.ready)
-                    __hip_atomic_fetch_add(P.ready + (u % kSlots) * kSlotStride, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                if (counted) add_dev(P.ready + (u % kSlots) * kSlotStride, 1u);
                 sh.last = 0;
+                if (first && tr) {
+                    tr[1] = sh.t_wait;
+                    tr[2] = sh.t_staged;
+                    tr[3] = sh.t_computed;
+                    tr[4] = __builtin_amdgcn_s_memrealtime();
+                }
             }
+            first = false;
             __syncthreads();
         }
         if (tr && threadIdx.x == 0) {
-            tr[2] = __builtin_amdgcn_s_memrealtime();
-            tr[3] = n_done;
+            tr[5] = __builtin_amdgcn_s_memrealtime();
+            tr[6] = n_done;
         }
     }
     if (cur >= 0) flush_best(P, sh.best, M);
     drain();
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(ctl + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = add_dev(ctl + 2, 1u);
         if (prev == gridDim.x - 1) {
             for (int i = kSlotStride; i < kSlotStride * (1 + n_phases * kSlots); i += kSlotStride)
-                __hip_atomic_store(ctl + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(ctl + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                st_dev(ctl + i, 0u);
+            st_dev(ctl + 2, 0u);
         }
     }
 }
@@ -958,7 +958,7 @@ struct sv_pass {
     sv::PhaseDesc *table;        // device
     unsigned *ctl;               // device: status, exit count, completion slots
     unsigned long long *argmax;  // device (or null): zeroed per run
-    unsigned long long *trace;   // device: [kMaxGrid][n_phases][4] timestamps
+    unsigned long long *trace;   // device: [kMaxGrid][n_phases][kTraceWords]
     bool tracing;
     std::vector<sv::PhaseDesc> host;
 };
@@ -979,7 +979,7 @@ extern "C" size_t sv_pass_workspace_bytes(const sv_phase *phases, int32_t n_phas
     }
     need += (static_cast<size_t>(n_phases) * sizeof(sv::PhaseDesc) + 255) / 256 * 256;
     need += (static_cast<size_t>(sv::kSlotStride) * (1 + n_phases * sv::kSlots) * 4 + 255) / 256 * 256;
-    need += (static_cast<size_t>(sv::kMaxGrid) * n_phases * 32 + 255) / 256 * 256;
+    need += (static_cast<size_t>(sv::kMaxGrid) * n_phases * sv::kTraceWords * 8 + 255) / 256 * 256;
     need += max_scratch;
     return need;
 }
@@ -1003,7 +1003,7 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
     const size_t ctl_bytes = (static_cast<size_t>(kSlotStride) * (1 + n_phases * kSlots) * 4 + 255) / 256 * 256;
     p->table = reinterpret_cast<PhaseDesc *>(b);
     p->ctl = reinterpret_cast<unsigned *>(b + table_bytes);
-    const size_t trace_bytes = (static_cast<size_t>(kMaxGrid) * n_phases * 32 + 255) / 256 * 256;
+    const size_t trace_bytes = (static_cast<size_t>(kMaxGrid) * n_phases * kTraceWords * 8 + 255) / 256 * 256;
     p->trace = reinterpret_cast<unsigned long long *>(b + table_bytes + ctl_bytes);
     p->tracing = false;
     uint8_t *scratch = b + table_bytes + ctl_bytes + trace_bytes;
@@ -1024,9 +1024,17 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
         }
         P.tile_count = reinterpret_cast<unsigned *>(scratch);
         P.partial = reinterpret_cast<float *>(scratch + kCounterBytes);
-        P.ready = p->ctl + kSlotStride * (1 + i * kSlots);
+        P.ready = (i + 1 < n_phases) ? p->ctl + kSlotStride * (1 + i * kSlots) : nullptr;
         P.wait = (i > 0) ? p->ctl + kSlotStride * (1 + (i - 1) * kSlots) : nullptr;
-        P.wait_target = (i > 0) ? static_cast<uint32_t>(p->host[i - 1].n_units) : 0u;
+        // The next phase reads only the requantised output: with K unsplit
+        // and no pairing, that comes from the units of matrix ep_src alone.
+        P.count_all = (P.S > 1 || P.ep_mode != SV_EP_QUANT) ? 1 : 0;
+        if (i > 0) {
+            const PhaseDesc &Q = p->host[i - 1];
+            P.wait_target = static_cast<uint32_t>(Q.count_all ? Q.n_units : Q.n_tiles);
+        } else {
+            P.wait_target = 0u;
+        }
         P.unit_base = tickets;
         tickets += static_cast<uint32_t>(P.n_units);
         if (P.argmax) p->argmax = P.argmax;
@@ -1112,7 +1120,7 @@ extern "C" int sv_pass_trace(sv_pass *p, int enable, uint64_t *host, size_t byte
     p->tracing = enable != 0;
     if (grid) *grid = p->grid;
     if (!host) return SV_OK;
-    const size_t need = static_cast<size_t>(p->grid) * p->n_phases * 32;
+    const size_t need = static_cast<size_t>(p->grid) * p->n_phases * kTraceWords * 8;
     SV_REQUIRE(bytes >= need, SV_ERR_WORKSPACE, "pass_trace: host buffer needs " + std::to_string(need) + " bytes");
     return hip_check(hipMemcpy(host, p->trace, need, hipMemcpyDeviceToHost), "pass_trace");
 }

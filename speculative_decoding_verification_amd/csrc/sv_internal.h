@@ -9,7 +9,7 @@
 
 #include <string>
 
-#include "../../include/specverify.h"
+#include "specverify.h"
 
 namespace sv {
 
@@ -36,6 +36,68 @@ struct Streams {
 bool streams_of(int32_t qtype, int64_t rows, int64_t cols, Streams *s);
 
 // --------------------------------------------------------- device helpers
+// Global-memory accesses through address-space-1 pointers.  A pointer read
+// from memory (a descriptor in LDS, say) is otherwise a generic pointer and
+// its loads become flat instructions, which also count against the LDS wait
+// counter.  Vector values move as clang vectors, not HIP's vector classes,
+// whose copy constructors would take the address back to generic.
+#define SV_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ __forceinline__ T gld(const T *p) {
+    return *(const SV_GLOBAL T *)p;
+}
+template <typename T>
+__device__ __forceinline__ void gst(T *p, T v) {
+    *(SV_GLOBAL T *)p = v;
+}
+__device__ __forceinline__ uint4 gld16(const void *p) {
+    const u32x4 v = *(const SV_GLOBAL u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 gld8(const void *p) {
+    const u32x2 v = *(const SV_GLOBAL u32x2 *)p;
+    return make_uint2(v.x, v.y);
+}
+// Streaming (non-temporal) loads for data read once.
+__device__ __forceinline__ uint4 gld16_nt(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load((const SV_GLOBAL u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 gld8_nt(const void *p) {
+    const u32x2 v = __builtin_nontemporal_load((const SV_GLOBAL u32x2 *)p);
+    return make_uint2(v.x, v.y);
+}
+
+// Cross-workgroup data of one launch moves through device-coherent accesses
+// (written through to, and read from, the level all XCDs share) instead of
+// fences: an agent-scope fence writes back or invalidates a whole L2, far too
+// costly once per unit.
+template <typename T>
+__device__ __forceinline__ void st_dev(T *p, T v) {
+    __hip_atomic_store((SV_GLOBAL T *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T *p) {
+    return __hip_atomic_load((SV_GLOBAL T *)const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T add_dev(T *p, T v) {
+    return __hip_atomic_fetch_add((SV_GLOBAL T *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T max_dev(T *p, T v) {
+    return __hip_atomic_fetch_max((SV_GLOBAL T *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T or_dev(T *p, T v) {
+    return __hip_atomic_fetch_or((SV_GLOBAL T *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's memory operations have completed.
+__device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
     _Float16 h;
     uint16_t b = static_cast<uint16_t>(h16);
