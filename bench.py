@@ -134,6 +134,59 @@ def per_phase_timing(stack, M, passes, cycles_per_ms):
     return out
 
 
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of a known size, so that a profiler
+    run over this script records FETCH_SIZE / WRITE_SIZE of a kernel whose
+    traffic is known exactly (the scale factor for the pass's counters)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    return nbytes
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pass_kernel_chain4b_m5_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decoding_verification_amd", "csrc", f)
+                  for f in ("matvec.hip", "sv_internal.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(config, M):
+    """HBM bytes per pass launch from the committed FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on the kernel sources as they are now (else
+    None)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    if fields.get("config") != config or fields.get("M") != str(M):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(keep, shape, seed, M, budget_s):
     import numpy as np
 
@@ -176,6 +229,8 @@ def main():
     ap.add_argument("--phase-breakdown", action="store_true", help="also time every phase as its own launch")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (the known-size kernel for counter scaling)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -224,11 +279,11 @@ def main():
     achieved = pass_bytes / (avg_us * 1e-6) / 1e9
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+        "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": recorded_traffic(args.config, hm),
         "kernel": f"sv::pass_kernel<{hm}> (all projection phases and the head in one launch)",
         "avg_launch_us": round(avg_us, 2), "p10_us": round(float(np.percentile(us, 10)), 2),
         "p90_us": round(float(np.percentile(us, 90)), 2), "launches": len(us),
-        "alg_bytes_per_launch": pass_bytes,
+        "alg_bytes_per_launch": pass_bytes, "kernel_source_sha256": kernel_source_hash(),
     }
     if args.phase_breakdown:
         per = per_phase_timing(stack, hm, 1, cpm)
@@ -236,6 +291,9 @@ def main():
             k: {"avg_us": round(float(np.mean(v)), 2), "launches_per_pass": len(v),
                 "gbps": round(stack.phase_bytes(k) / (np.mean(v) * 1e-6) / 1e9, 1) if stack.phase_bytes(k) else None}
             for k, v in per.items()}
+
+    if args.copy_calibration:
+        copy_calibration()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -263,6 +321,7 @@ def main():
                                f"Q6_K head {shape.vocab}x{shape.hidden}, greedy acceptance",
                    "M": hm, "drafts": hm - 1, "bytes_per_pass": pass_bytes},
         "pct_hbm_peak": round(head_row["pct_hbm_peak"], 2),
+        "growth_t5_over_t1": next((round(r["t_over_t1"], 4) for r in sweep if r["M"] == 5 and r["t_over_t1"]), None),
         "positions_per_s": round(head_row["positions_per_s"], 1),
         "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in sweep],
         "roofline": roofline,
