@@ -8,30 +8,28 @@
 // loads are reused across weight rows, and one launch carries the phases of
 // a cycle separated by grid-wide synchronisation).
 //
-// Work decomposition.  A phase (one or up to three matrices sharing an
-// input) is cut into units = (row tile, K chunk, matrix):
-//  * K is cut into 32-element sub-blocks.  A group of g lanes (g = 32 or
-//    16, fixed by K alone) shares one row; lane j of the group takes
-//    sub-blocks j, j+g, j+2g, ... of the chunk, so g lanes read g
-//    consecutive 16-byte records of a row: one contiguous aligned run.
-//  * Each lane carries R = 4 rows.  The activations of its sub-block are
-//    read from LDS once per step and reused for the R rows; the weights are
-//    read from HBM once and reused for all M positions.
-//  * A row tile has 64/g * 4 waves * R rows (32 or 64); the K axis is split
-//    into S(K) chunks so that even the smallest phases offer hundreds of
-//    units to the 256 compute units.
+// Work decomposition.  A phase (one to three matrices sharing an input) is
+// cut into units = (32-row tile, K chunk, matrix):
+//  * K is walked in steps of 256 elements (one K-quant super-block, eight
+//    Q8_0 blocks); a chunk is at most 12 steps, so S(K) = ceil(steps / 12)
+//    depends on K alone.  Each of the four waves takes <= 3 of the chunk's
+//    steps.
+//  * Lane j of an 8-lane row group reads sub-block 8t + j of four rows: the
+//    group reads 128 contiguous bytes of a row, and each weight record is
+//    read once and reused from registers for all M positions.  The input
+//    chunk is staged in LDS once per unit.
 // Arithmetic.  Integer block sums come from v_dot4 (exact); each block's
 // fp32 combine is a fixed sequence of operations per (row, position); a lane
-// adds its blocks in increasing order, the g lanes of a group are combined by
-// a butterfly, and the S chunk partials are added in chunk order by the last
-// unit of the row tile to finish.  Nothing depends on M or on which
-// workgroup ran which unit, so every output row is bit-identical to the same
-// row computed alone, and runs are deterministic.
+// adds its blocks in increasing order, the 8 lanes of a group are combined
+// by a butterfly, the four waves in wave order and the K chunks in chunk
+// order.  Nothing depends on M or on which workgroup ran which unit, so every
+// output row is bit-identical to the same row computed alone, and runs are
+// deterministic.
 // Scheduling.  Single calls launch one workgroup per unit.  A whole pass
 // runs as one persistent launch sized to the number of workgroups the GPU
 // holds at once: the units of each phase are dealt round-robin, and a
-// workgroup issues a unit's first weight loads before it waits until the
-// phase its input comes from has finished.  All waits are bounded.
+// workgroup issues a unit's weight loads before it waits until the phase its
+// input comes from has handed off.  All waits are bounded.
 #include <algorithm>
 #include <vector>
 
