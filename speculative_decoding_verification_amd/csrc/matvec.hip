@@ -54,6 +54,7 @@ struct PhaseDesc {
     int32_t N, K, wrows;
     int32_t S, steps, n_tiles, per_tile, n_units, chunk_sub;
     int32_t count_all;        // 0: only units of matrix ep_src feed the next phase
+    int32_t fused;            // 1: a unit covers both matrices of a Q4_K gate/up pair
     uint64_t o1, o2, o3;
     const int32_t *row_ids;
     const int8_t *aq;
@@ -86,9 +87,13 @@ struct WRaw<SV_Q8_0> {
     uint4 q0, q1;
     uint32_t d;
 };
+// The Q4_K super-block header (16 bytes per row and step) is spread over a
+// quad of lanes, one dword each, and shared at decode time with quad
+// permutes instead of every lane holding a copy.
 template <>
 struct WRaw<SV_Q4_K> {
-    uint4 q, h;
+    uint4 q;
+    uint32_t h;   // header dword (lane & 3): d|dmin, scale/min bytes 0-3, 4-7, 8-11
 };
 template <>
 struct WRaw<SV_Q6_K> {
@@ -107,7 +112,7 @@ __device__ __forceinline__ void load_w(WRaw<QT> &r, const uint8_t *__restrict__ 
         r.d = gld(reinterpret_cast<const uint16_t *>(w + P.o1 + (row * nsub + s) * 2));
     } else if constexpr (QT == SV_Q4_K) {
         r.q = gld16_nt(w + (row * nsub + s) * 16);
-        r.h = gld16(w + P.o1 + (row * (K >> 8) + (s >> 3)) * 16);
+        r.h = gld(reinterpret_cast<const uint32_t *>(w + P.o1 + (row * (K >> 8) + (s >> 3)) * 16) + (s & 3));
     } else {
         r.l = gld16_nt(w + (row * nsub + s) * 16);
         r.h = gld8_nt(w + P.o1 + (row * nsub + s) * 8);
@@ -124,6 +129,12 @@ struct WDec {
     int32_t i0, i1;  // Q6_K: the two int8 sub-scales
 };
 
+// Value of quad lane i (CTRL = i * 0x55) of v in every lane of each quad.
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
 template <int QT>
 __device__ __forceinline__ void decode_w(WDec &o, const WRaw<QT> &r, int j8) {
     if constexpr (QT == SV_Q8_0) {
@@ -139,17 +150,19 @@ __device__ __forceinline__ void decode_w(WDec &o, const WRaw<QT> &r, int j8) {
         }
         // 6-bit sub-scale and min of sub-block j8 from the 12 packed bytes
         // (header dwords y, z, w) of the ggml Q4_K layout.
+        const uint32_t hx = quad_bcast<0x00>(r.h), hy = quad_bcast<0x55>(r.h);
+        const uint32_t hz = quad_bcast<0xAA>(r.h), hw = quad_bcast<0xFF>(r.h);
         const uint32_t sh = 8u * (j8 & 3);
         uint32_t sc, mn;
         if (j8 < 4) {
-            sc = __builtin_amdgcn_ubfe(r.h.y, sh, 6);
-            mn = __builtin_amdgcn_ubfe(r.h.z, sh, 6);
+            sc = __builtin_amdgcn_ubfe(hy, sh, 6);
+            mn = __builtin_amdgcn_ubfe(hz, sh, 6);
         } else {
-            sc = __builtin_amdgcn_ubfe(r.h.w, sh, 4) | (__builtin_amdgcn_ubfe(r.h.y, sh + 6, 2) << 4);
-            mn = __builtin_amdgcn_ubfe(r.h.w, sh + 4, 4) | (__builtin_amdgcn_ubfe(r.h.z, sh + 6, 2) << 4);
+            sc = __builtin_amdgcn_ubfe(hw, sh, 4) | (__builtin_amdgcn_ubfe(hy, sh + 6, 2) << 4);
+            mn = __builtin_amdgcn_ubfe(hw, sh + 4, 4) | (__builtin_amdgcn_ubfe(hz, sh + 6, 2) << 4);
         }
-        const float d = half_bits_to_float(r.h.x & 0xFFFFu);
-        const float dmin = half_bits_to_float(r.h.x >> 16);
+        const float d = half_bits_to_float(hx & 0xFFFFu);
+        const float dmin = half_bits_to_float(hx >> 16);
         o.s0 = d * static_cast<float>(sc);
         o.s1 = dmin * static_cast<float>(mn);
     } else {
@@ -447,13 +460,15 @@ struct MG {
     static constexpr int value = M > 8 ? 8 : M;
 };
 
-// One unit: rows [row0, row0 + 32) x the K chunk `chunk`, for matrices
-// [mat_lo, mat_hi).  Wave w takes steps [w0, w1) of the chunk (one step = 8
-// sub-blocks per row, one 256-element super-block of a K-quant); lane j of
-// row group grp reads sub-block 8 t + j of rows row0 + 4 grp + p, p < 4.
-template <int QT, int M>
-__device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart, int CS,
-                         Shared<M> &sh, bool do_wait, unsigned *status) {
+// One unit: rows [row0, row0 + 32) x the K chunk `chunk`, for NM matrices
+// from `mat` (NM = 2: both matrices of a gate/up pair, so the pair's
+// product forms inside the unit).  Wave w takes steps [w0, w1) of the chunk
+// of each matrix (one step = 8 sub-blocks per row, one 256-element
+// super-block of a K-quant); lane j of row group grp reads sub-block 8 t + j
+// of rows row0 + 4 grp + p, p < 4.
+template <int QT, int M, int NM>
+__device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart,
+                                         int CS, Shared<M> &sh, bool do_wait, unsigned *status) {
     constexpr int MGV = MG<M>::value;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 3, jl = lane & 7;
@@ -482,15 +497,18 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
         srow[p] = (sr < 0 || sr >= P.wrows) ? 0 : sr;
     }
     // Every weight record of this unit is requested before waiting for the
-    // input (at most kMaxWaveSteps steps per wave).
-    const uint8_t *__restrict__ w = P.w[mat];
-    WRaw<QT> raw[kMaxWaveSteps][kR];
+    // input (at most kMaxWaveSteps steps per wave and matrix).
+    WRaw<QT> raw[NM][kMaxWaveSteps][kR];
 #pragma unroll
-    for (int t = 0; t < kMaxWaveSteps; t++) {
-        const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
-        if (w0 + t < w1 && sb < nsub) {
+    for (int mm = 0; mm < NM; mm++) {
+        const uint8_t *__restrict__ w = P.w[mat + mm];
 #pragma unroll
-            for (int p = 0; p < kR; p++) load_w<QT>(raw[t][p], w, P, srow[p], sb);
+        for (int t = 0; t < kMaxWaveSteps; t++) {
+            const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
+            if (w0 + t < w1 && sb < nsub) {
+#pragma unroll
+                for (int p = 0; p < kR; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sb);
+            }
         }
     }
     // the epilogue's norm weight of this thread's row, fetched off the
@@ -506,11 +524,13 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
         if (threadIdx.x == 0) sh.t_wait = __builtin_amdgcn_s_memrealtime();
         need_rs = true;
     }
-    float acc[kR][M];
+    float acc[NM][kR][M];
 #pragma unroll
-    for (int p = 0; p < kR; p++)
+    for (int mm = 0; mm < NM; mm++)
 #pragma unroll
-        for (int m = 0; m < M; m++) acc[p][m] = 0.0f;
+        for (int p = 0; p < kR; p++)
+#pragma unroll
+            for (int m = 0; m < M; m++) acc[mm][p][m] = 0.0f;
 #pragma unroll
     for (int m0 = 0; m0 < M; m0 += MGV) {
         const int mg = min(MGV, M - m0);
@@ -523,16 +543,20 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
             const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
             if (w0 + t < w1 && sb < nsub) {
                 const int sl = static_cast<int>(sb - s_begin);
-                WDec dec[kR];
 #pragma unroll
-                for (int p = 0; p < kR; p++) decode_w<QT>(dec[p], raw[t][p], jl);
+                for (int mm = 0; mm < NM; mm++) {
+                    WDec dec[kR];
 #pragma unroll
-                for (int m = 0; m < MGV; m++) {
-                    if (m0 + m < M) {
-                        ARec ar;
-                        read_act(ar, act + m * CS * kActRec, CS, sl);
+                    for (int p = 0; p < kR; p++) decode_w<QT>(dec[p], raw[mm][t][p], jl);
 #pragma unroll
-                        for (int p = 0; p < kR; p++) acc[p][m0 + m] = block_term<QT>(dec[p], ar, acc[p][m0 + m]);
+                    for (int m = 0; m < MGV; m++) {
+                        if (m0 + m < M) {
+                            ARec ar;
+                            read_act(ar, act + m * CS * kActRec, CS, sl);
+#pragma unroll
+                            for (int p = 0; p < kR; p++)
+                                acc[mm][p][m0 + m] = block_term<QT>(dec[p], ar, acc[mm][p][m0 + m]);
+                        }
                     }
                 }
             }
@@ -542,34 +566,37 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
     // Lanes of a row group: butterfly; waves: partials through LDS, added in
     // wave order.
 #pragma unroll
-    for (int p = 0; p < kR; p++)
+    for (int mm = 0; mm < NM; mm++)
 #pragma unroll
-        for (int m = 0; m < M; m++) {
-            float v = acc[p][m];
+        for (int p = 0; p < kR; p++)
 #pragma unroll
-            for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-            if (jl == 0) wpart[(wave * M + m) * kRows + grp * kR + p] = v;
-        }
+            for (int m = 0; m < M; m++) {
+                float v = acc[mm][p][m];
+#pragma unroll
+                for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+                if (jl == 0) wpart[((wave * NM + mm) * M + m) * kRows + grp * kR + p] = v;
+            }
     __syncthreads();
     // chunk value of (m, row) = ((w0 + w1) + w2) + w3.  A tile is final here
-    // unless K is split over units or the epilogue pairs two matrices.
-    const bool split = P.S > 1 || pair;
-    for (int i = threadIdx.x; i < M * kRows; i += kThreads) {
-        const int m = i / kRows, r = i % kRows;
-        float v = wpart[(0 * M + m) * kRows + r];
-        v += wpart[(1 * M + m) * kRows + r];
-        v += wpart[(2 * M + m) * kRows + r];
-        v += wpart[(3 * M + m) * kRows + r];
+    // unless K is split over units or a pair's matrices sit in two units.
+    const bool split = P.S > 1 || (pair && NM == 1);
+    for (int i = threadIdx.x; i < NM * M * kRows; i += kThreads) {
+        const int mm = i / (M * kRows), r2 = i % (M * kRows), m = r2 / kRows, r = r2 % kRows;
+        float v = wpart[((0 * NM + mm) * M + m) * kRows + r];
+        v += wpart[((1 * NM + mm) * M + m) * kRows + r];
+        v += wpart[((2 * NM + mm) * M + m) * kRows + r];
+        v += wpart[((3 * NM + mm) * M + m) * kRows + r];
         if (!split) {
-            ystage[(mat * M + m) * kRows + r] = v * sh.rscale[m];
+            ystage[((mat + mm) * M + m) * kRows + r] = v * sh.rscale[m];
         } else {
             const int64_t rr = row0 + r;
-            if (rr < P.N) st_dev(P.partial + ((static_cast<int64_t>(mat) * P.S + chunk) * M + m) * P.N + rr, v);
+            if (rr < P.N)
+                st_dev(P.partial + ((static_cast<int64_t>(mat + mm) * P.S + chunk) * M + m) * P.N + rr, v);
         }
     }
     if (!split) {
         __syncthreads();
-        finish_tile<M>(P, ystage, row0, mat, mat + 1, mat == P.ep_src, g_row, sh);
+        finish_tile<M>(P, ystage, row0, mat, mat + NM, NM == 2 || mat == P.ep_src, g_row, sh);
         return true;
     }
     // K split over units: the last unit of the tile to finish adds the chunk
@@ -607,9 +634,12 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
 template <int M>
 __device__ __forceinline__ bool dispatch_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart,
                                               int CS, Shared<M> &sh, bool do_wait, unsigned *status) {
-    if (P.qtype == SV_Q4_K) return run_unit<SV_Q4_K, M>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
-    if (P.qtype == SV_Q6_K) return run_unit<SV_Q6_K, M>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
-    return run_unit<SV_Q8_0, M>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
+    if (P.qtype == SV_Q4_K) {
+        if (P.fused) return run_unit<SV_Q4_K, M, 2>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
+        return run_unit<SV_Q4_K, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
+    }
+    if (P.qtype == SV_Q6_K) return run_unit<SV_Q6_K, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
+    return run_unit<SV_Q8_0, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
 }
 
 __device__ __forceinline__ void flush_best(const PhaseDesc &P, unsigned long long *best, int M) {
@@ -622,7 +652,7 @@ __device__ __forceinline__ void flush_best(const PhaseDesc &P, unsigned long lon
 }
 
 // LDS layout of a workgroup: act chunk [MG][CS * kActRec] | ystage
-// [3][M][kRows] fp32 | wave partials [4][M][kRows] fp32.
+// [3][M][kRows] fp32 | wave partials [4][2][M][kRows] fp32.
 template <int M>
 __device__ __forceinline__ void lds_parts(uint8_t *smem, int CS, float *&ystage, float *&wpart) {
     ystage = reinterpret_cast<float *>(smem + MG<M>::value * CS * kActRec);
@@ -760,7 +790,10 @@ static void decompose(PhaseDesc &P) {
     P.steps = static_cast<int>((nsub + 7) / 8);
     P.S = std::max(1, (P.steps + kMaxChunkSteps - 1) / kMaxChunkSteps);
     P.n_tiles = static_cast<int>((static_cast<int64_t>(P.N) + kRows - 1) / kRows);
-    P.per_tile = P.S * P.n_w;
+    // A Q4_K gate/up pair runs as one unit per (tile, chunk): its records
+    // leave room in registers for both matrices.
+    P.fused = (P.ep_mode == SV_EP_PAIR && P.qtype == SV_Q4_K && P.n_w == 2) ? 1 : 0;
+    P.per_tile = P.S * (P.fused ? 1 : P.n_w);
     P.n_units = P.n_tiles * P.per_tile;
     P.chunk_sub = ((P.steps + P.S - 1) / P.S) * 8;
 }
@@ -768,10 +801,10 @@ static void decompose(PhaseDesc &P) {
 static size_t lds_bytes(int M, int CS) {
     const int mg = M > 8 ? 8 : M;
     return static_cast<size_t>(mg) * CS * kActRec + static_cast<size_t>(3) * M * kRows * 4 +
-           static_cast<size_t>(4) * M * kRows * 4;
+           static_cast<size_t>(8) * M * kRows * 4;
 }
 
-static bool needs_partials(const PhaseDesc &P) { return P.S > 1 || P.ep_mode == SV_EP_PAIR; }
+static bool needs_partials(const PhaseDesc &P) { return P.S > 1 || (P.ep_mode == SV_EP_PAIR && !P.fused); }
 
 static size_t partial_bytes(const PhaseDesc &P, int M) {
     if (!needs_partials(P)) return 0;
@@ -904,7 +937,10 @@ extern "C" size_t sv_matvec_workspace_bytes(const sv_weight *W, int32_t n_w, con
     sv::PhaseDesc P;
     if (sv::make_phase(P, W, n_w, A, nullptr, nullptr, nullptr, 0, nullptr) != SV_OK) return 0;
     // sized for any epilogue: two matrices may be paired
-    if (n_w == 2) P.ep_mode = SV_EP_PAIR;
+    if (n_w == 2) {
+        P.ep_mode = SV_EP_PAIR;
+        sv::decompose(P);
+    }
     return sv::phase_scratch(P, A->M);
 }
 

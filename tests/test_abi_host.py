@@ -150,16 +150,18 @@ def test_head_and_accept_rejects():
 
 def test_workspace_sizes():
     """K is cut into ceil(steps / 12) chunks of 256-element steps; partial sums
-    (after a fixed 256 KiB counter region) are needed when K is split or two
-    matrices may be paired, and nothing otherwise."""
+    (after a fixed 256 KiB counter region) are needed when K is split, or
+    when two matrices may be paired and a unit cannot hold both (anything but
+    Q4_K), and nothing otherwise."""
     L = sv.lib()
     for rows, cols, qt, n_w, M, S in [(2560, 2560, 12, 3, 5, 1), (2560, 9728, 14, 1, 5, 4), (9728, 2560, 12, 2, 16, 1),
-                                      (5120, 17408, 14, 1, 5, 6), (17408, 5120, 12, 1, 8, 2)]:
+                                      (5120, 17408, 14, 1, 5, 6), (17408, 5120, 12, 1, 8, 2),
+                                      (2560, 2560, 14, 2, 5, 1), (17408, 5120, 12, 2, 5, 2)]:
         steps = -(-cols // 256)
         assert -(-steps // 12) == S
         W = (sv.Weight * n_w)(*([_w(qt=qt, rows=rows, cols=cols)] * n_w))
         need = L.sv_matvec_workspace_bytes(W, n_w, ctypes.byref(_act(M=M, K=cols)))
-        if S == 1 and n_w != 2:
+        if S == 1 and (n_w != 2 or qt == 12):
             assert need == 0
         else:
             assert need == 256 * 1024 + n_w * S * M * rows * 4
