@@ -50,7 +50,7 @@ constexpr int kMaxGrid = 1024;          // most workgroups a pass launches
 // Device-side description of one phase.
 struct PhaseDesc {
     const uint8_t *w[3];
-    int32_t qtype, n_w;
+    int32_t qtype, n_w, M;
     int32_t N, K, wrows;
     int32_t S, steps, n_tiles, per_tile, n_units, chunk_sub;
     int32_t count_all;        // 0: only units of matrix ep_src feed the next phase
@@ -661,7 +661,7 @@ __device__ __forceinline__ void lds_parts(uint8_t *smem, int CS, float *&ystage,
 
 // One workgroup per unit of a single phase.
 template <int M>
-__global__ __launch_bounds__(kThreads) void phase_kernel(PhaseDesc P, int CS) {
+__global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void phase_kernel(PhaseDesc P, int CS) {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ Shared<M> sh;
     float *ystage, *wpart;
@@ -680,7 +680,7 @@ constexpr int kTraceWords = 8;
 // finished units.  The last workgroup to exit returns every counter but the
 // status to zero, so the next run starts clean without a reset launch.
 template <int M>
-__global__ __launch_bounds__(kThreads) void pass_kernel(const PhaseDesc *__restrict__ table, int n_phases,
+__global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const PhaseDesc *__restrict__ table, int n_phases,
                                                         unsigned *ctl, int CS, unsigned long long *argmax,
                                                         unsigned long long *trace) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -790,9 +790,9 @@ static void decompose(PhaseDesc &P) {
     P.steps = static_cast<int>((nsub + 7) / 8);
     P.S = std::max(1, (P.steps + kMaxChunkSteps - 1) / kMaxChunkSteps);
     P.n_tiles = static_cast<int>((static_cast<int64_t>(P.N) + kRows - 1) / kRows);
-    // A Q4_K gate/up pair runs as one unit per (tile, chunk): its records
-    // leave room in registers for both matrices.
-    P.fused = (P.ep_mode == SV_EP_PAIR && P.qtype == SV_Q4_K && P.n_w == 2) ? 1 : 0;
+    // A Q4_K gate/up pair runs as one unit per (tile, chunk) for M <= 8: its
+    // records leave room in registers for both matrices.
+    P.fused = (P.ep_mode == SV_EP_PAIR && P.qtype == SV_Q4_K && P.n_w == 2 && P.M <= 8) ? 1 : 0;
     P.per_tile = P.S * (P.fused ? 1 : P.n_w);
     P.n_units = P.n_tiles * P.per_tile;
     P.chunk_sub = ((P.steps + P.S - 1) / P.S) * 8;
@@ -859,6 +859,7 @@ static int make_phase(PhaseDesc &P, const sv_weight *W, int32_t n_w, const sv_ac
     P.wrows = static_cast<int32_t>(W[0].rows);
     P.N = static_cast<int32_t>(row_ids ? n_rows : W[0].rows);
     P.K = static_cast<int32_t>(A->K);
+    P.M = A->M;
     Streams s;
     streams_of(W[0].qtype, W[0].rows, W[0].cols, &s);
     P.o1 = s.off[1];
