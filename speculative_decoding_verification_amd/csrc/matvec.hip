@@ -257,17 +257,26 @@ __device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target,
         const int lane = threadIdx.x;
         unsigned n = 0;
         bool ok = true;
+        // two polls in flight: the next read is issued before the previous
+        // one is examined, so an update is seen about half a round trip
+        // sooner than with one read at a time
+        // every lane reads (lanes >= kSlots repeat the first slots), so no
+        // branch hides the loads from the wait-count bookkeeping
+        const unsigned *slot = ctr + (lane & (kSlots - 1)) * kSlotStride;
+        unsigned a = ld_dev(slot);
         for (;;) {
-            unsigned v = (lane < kSlots) ? ld_dev(ctr + lane * kSlotStride) : 0u;
+            __builtin_amdgcn_s_sleep(4);
+            const unsigned b = ld_dev(slot);
+            unsigned v = (lane < kSlots) ? a : 0u;
 #pragma unroll
             for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
             v = __shfl(v, 0, 64);
             if (v >= target) break;
-            if (ld_dev(status) != 0u || ++n > kSpinLimit) {
+            if (++n > kSpinLimit || ((n & 63u) == 0u && ld_dev(status) != 0u)) {
                 ok = false;
                 break;
             }
-            __builtin_amdgcn_s_sleep(2);
+            a = b;
         }
         if (lane == 0) {
             if (!ok) or_dev(status, 1u);
@@ -287,24 +296,9 @@ constexpr int kStageHalf = 6;   // >= 8 positions * 96 sub-blocks * 2 halves / 2
 constexpr int kStageRec = 3;    // >= 8 * 96 / 256
 constexpr int kPartsPerLane = 9;  // >= 544 partials / 64 lanes
 
-__device__ __forceinline__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int64_t s0, int cs, int CS,
-                          float *rs, int M) {
+__device__ __forceinline__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int64_t s0, int cs,
+                                          int CS) {
     const int64_t K = P.K, nsub = K >> 5;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // RMS partials: two positions per wave per round (positions wave + 4 k)
-    float pv[2][kPartsPerLane];
-    const bool do_rs = rs && P.in_parts;
-    if (do_rs) {
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const int m = wave + 4 * k;
-#pragma unroll
-            for (int j = 0; j < kPartsPerLane; j++) {
-                const int i = lane + 64 * j;
-                pv[k][j] = (m < M && i < P.n_parts) ? gld(P.in_parts + m * P.n_parts + i) : 0.0f;
-            }
-        }
-    }
     const int nhalf = mg * cs * 2, nrec = mg * cs;
     // named registers, not arrays: a private array here ends up in scratch
     uint4 h0, h1, h2, h3, h4, h5;
@@ -361,34 +355,72 @@ __device__ __forceinline__ void stage_act(uint8_t *act, const PhaseDesc &P, int 
     }
     SV_STR(0, d0, x0) SV_STR(1, d1, x1) SV_STR(2, d2, x2)
 #undef SV_STR
-    if (rs) {
+}
+
+// Sums over lanes with data-parallel primitives (no LDS traffic), in a fixed
+// order.  DPP controls: quad_perm, row_shl:n = 0x100 + n, row_ror:n = 0x120 + n.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// ((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7)) of each group of eight
+// lanes, in the group's lane 0.
+__device__ __forceinline__ float group8_sum(float v) {
+    v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f<0x104>(v);   // row_shl:4
+    return v;
+}
+// Sum of the 64 lanes of the wave (every lane gets it): quads, then rows
+// of 16, then the four rows in order.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x124>(v);   // row_ror:4
+    v += dpp_f<0x128>(v);   // row_ror:8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return ((r0 + r1) + r2) + r3;
+}
+
+// RMS factors r = 1 / sqrt(sum / K + eps) of the input rows from its
+// per-block sums of squares.  Wave w takes positions w + 4 k; lane l adds
+// partials l, l + 64, ... in order, then wave_sum: a fixed order that
+// depends only on the number of partials.  Every load is issued before any
+// is used (from a valid address, selected afterwards: a conditional load
+// with an else value makes the compiler wait for it before the next one).
+struct RmsParts {
+    float v[2][kPartsPerLane];
+};
+
+__device__ __forceinline__ void rms_load(RmsParts &pv, const PhaseDesc &P, int round, int M) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const int m = wave + 4 * k;
-            if (k == 2 && do_rs && M > 8) {
-                // positions 8..15: second round of partial loads
+    for (int k = 0; k < 2; k++) {
+        const int m = wave + 4 * (2 * round + k);
 #pragma unroll
-                for (int kk = 0; kk < 2; kk++) {
-                    const int mm = wave + 4 * (kk + 2);
+        for (int j = 0; j < kPartsPerLane; j++) {
+            const int i = lane + 64 * j;
+            const bool ok = m < M && i < P.n_parts;
+            const float x = gld(P.in_parts + (ok ? m * P.n_parts + i : 0));
+            pv.v[k][j] = ok ? x : 0.0f;
+        }
+    }
+}
+
+__device__ __forceinline__ void rms_store(const RmsParts &pv, const PhaseDesc &P, int round, int M, float *rs) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-                    for (int j = 0; j < kPartsPerLane; j++) {
-                        const int i = lane + 64 * j;
-                        pv[kk][j] = (mm < M && i < P.n_parts) ? gld(P.in_parts + mm * P.n_parts + i) : 0.0f;
-                    }
-                }
-            }
-            if (m < M) {
-                float r = 1.0f;
-                if (do_rs) {
-                    float s = 0.0f;
+    for (int k = 0; k < 2; k++) {
+        const int m = wave + 4 * (2 * round + k);
+        if (m < M) {
+            float t = 0.0f;
 #pragma unroll
-                    for (int j = 0; j < kPartsPerLane; j++) s += pv[k & 1][j];
-#pragma unroll
-                    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-                    r = 1.0f / sqrtf(s / static_cast<float>(P.K) + P.eps);
-                }
-                if (lane == 0) rs[m] = r;
-            }
+            for (int j = 0; j < kPartsPerLane; j++) t += pv.v[k][j];
+            const float tot = wave_sum(t);
+            if (lane == 0) rs[m] = 1.0f / sqrtf(tot / static_cast<float>(P.K) + P.eps);
         }
     }
 }
@@ -468,7 +500,7 @@ struct MG {
 // of rows row0 + 4 grp + p, p < 4.
 template <int QT, int M, int NM>
 __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart,
-                                         int CS, Shared<M> &sh, bool do_wait, unsigned *status) {
+                                         int CS, Shared<M> &sh, bool do_wait, unsigned *status, bool restage) {
     constexpr int MGV = MG<M>::value;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 3, jl = lane & 7;
@@ -534,9 +566,13 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
 #pragma unroll
     for (int m0 = 0; m0 < M; m0 += MGV) {
         const int mg = min(MGV, M - m0);
-        __syncthreads();
-        stage_act(act, P, m0, mg, s_begin, cs, CS, (need_rs && m0 == 0) ? sh.rscale : nullptr, M);
-        __syncthreads();
+        // the chunk staged for the previous unit of this phase may be the
+        // same one (then it is still in LDS)
+        if (restage || M > MGV) {
+            __syncthreads();
+            stage_act(act, P, m0, mg, s_begin, cs, CS);
+            __syncthreads();
+        }
         if (do_wait && m0 == 0 && threadIdx.x == 0) sh.t_staged = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
         for (int t = 0; t < kMaxWaveSteps; t++) {
@@ -563,19 +599,32 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
         }
     }
     if (do_wait && threadIdx.x == 0) sh.t_computed = __builtin_amdgcn_s_memrealtime();
-    // Lanes of a row group: butterfly; waves: partials through LDS, added in
-    // wave order.
+    // The input's RMS factors (first unit of a phase) are formed now, with
+    // the weight registers free: their loads are in flight during the
+    // reduction below.
+    RmsParts pv;
+    const bool rms = need_rs && P.in_parts;
+    if (rms) rms_load(pv, P, 0, M);
+    // Lanes of a row group: fixed-order sum; waves: partials through LDS,
+    // added in wave order.
 #pragma unroll
     for (int mm = 0; mm < NM; mm++)
 #pragma unroll
         for (int p = 0; p < kR; p++)
 #pragma unroll
             for (int m = 0; m < M; m++) {
-                float v = acc[mm][p][m];
-#pragma unroll
-                for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+                const float v = group8_sum(acc[mm][p][m]);
                 if (jl == 0) wpart[((wave * NM + mm) * M + m) * kRows + grp * kR + p] = v;
             }
+    if (rms) {
+        rms_store(pv, P, 0, M, sh.rscale);
+        if (M > 8) {
+            rms_load(pv, P, 1, M);
+            rms_store(pv, P, 1, M, sh.rscale);
+        }
+    } else if (need_rs && threadIdx.x < M) {
+        sh.rscale[threadIdx.x] = 1.0f;
+    }
     __syncthreads();
     // chunk value of (m, row) = ((w0 + w1) + w2) + w3.  A tile is final here
     // unless K is split over units or a pair's matrices sit in two units.
@@ -617,7 +666,11 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
             const float *src = P.partial + (static_cast<int64_t>(mt) * P.S * M + m) * P.N + row0 + r;
             float v[kMaxS];
 #pragma unroll
-            for (int c = 0; c < kMaxS; c++) v[c] = (c < P.S) ? ld_dev(src + static_cast<int64_t>(c) * M * P.N) : 0.0f;
+            for (int c = 0; c < kMaxS; c++) {
+                // every chunk's partial is requested before any is used
+                const float x = ld_dev(src + static_cast<int64_t>(c < P.S ? c : 0) * M * P.N);
+                v[c] = c < P.S ? x : 0.0f;
+            }
 #pragma unroll
             for (int c = 0; c < kMaxS; c++)
                 if (c < P.S) s += v[c];
@@ -633,13 +686,15 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
 
 template <int M>
 __device__ __forceinline__ bool dispatch_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart,
-                                              int CS, Shared<M> &sh, bool do_wait, unsigned *status) {
+                                              int CS, Shared<M> &sh, bool do_wait, unsigned *status,
+                                              bool restage = true) {
     if (P.qtype == SV_Q4_K) {
-        if (P.fused) return run_unit<SV_Q4_K, M, 2>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
-        return run_unit<SV_Q4_K, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
+        if (P.fused) return run_unit<SV_Q4_K, M, 2>(P, unit, act, ystage, wpart, CS, sh, do_wait, status, restage);
+        return run_unit<SV_Q4_K, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status, restage);
     }
-    if (P.qtype == SV_Q6_K) return run_unit<SV_Q6_K, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
-    return run_unit<SV_Q8_0, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status);
+    if (P.qtype == SV_Q6_K)
+        return run_unit<SV_Q6_K, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status, restage);
+    return run_unit<SV_Q8_0, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status, restage);
 }
 
 __device__ __forceinline__ void flush_best(const PhaseDesc &P, unsigned long long *best, int M) {
@@ -710,8 +765,12 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const Ph
         unsigned long long *tr = trace ? trace + (static_cast<size_t>(b) * n_phases + p) * kTraceWords : nullptr;
         if (tr && threadIdx.x == 0) tr[0] = __builtin_amdgcn_s_memrealtime();
         unsigned n_done = 0;
+        int staged = -1;   // first step of the K chunk in LDS (this phase)
         for (; u < nu; u += G) {
-            ok = dispatch_unit<M>(P, static_cast<int>(u), smem, ystage, wpart, CS, sh, first, status);
+            const int chunk = static_cast<int>(u % P.per_tile) % P.S;
+            const int c0 = static_cast<int>(static_cast<int64_t>(chunk) * P.steps / P.S);
+            ok = dispatch_unit<M>(P, static_cast<int>(u), smem, ystage, wpart, CS, sh, first, status, c0 != staged);
+            staged = c0;
             if (!ok) break;
             n_done++;
             // Only units whose outputs the next phase reads are handed off
