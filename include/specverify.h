@@ -249,14 +249,16 @@ int sv_pass_run(const sv_pass *pass, void *stream);
 int sv_pass_status(const sv_pass *pass, uint32_t *status);
 
 /* Profiling.  enable != 0 makes later runs record, per workgroup and phase,
- * eight words: the 100 MHz real-time counter when the workgroup reached the
- * phase, when its input became ready, when its first unit had staged the
- * input, finished its dot products, and was done (outputs written and
- * counted), when its last unit was done, then the number of units it ran
- * and an unused word ([grid][n_phases][8], zero rows for phases in which a
- * workgroup had no unit).  With host != NULL the last run's record is
- * copied there (synchronous; bytes >= grid * n_phases * 64).  *grid (may be
- * NULL) receives the number of workgroups a run launches. */
+ * twelve words: the 100 MHz real-time counter when the workgroup reached
+ * the phase, when its input became ready, when its first unit had staged
+ * the input, finished its dot products, and was done (outputs written and
+ * counted), when its last unit was done, the number of units it ran, when
+ * the first unit had its output rows combined and when its epilogue was
+ * written (0 if that unit did not run the epilogue), and three unused words
+ * ([grid][n_phases][12], zero rows for phases in which a workgroup had no
+ * unit).  With host != NULL the last run's record is copied there
+ * (synchronous; bytes >= grid * n_phases * 96).  *grid (may be NULL)
+ * receives the number of workgroups a run launches. */
 int sv_pass_trace(sv_pass *pass, int enable, uint64_t *host, size_t bytes, int32_t *grid);
 
 void sv_pass_destroy(sv_pass *pass);

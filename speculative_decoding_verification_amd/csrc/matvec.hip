@@ -243,7 +243,7 @@ struct Shared {
     unsigned long long best[SV_MAX_M];
     int last;
     unsigned abort;
-    unsigned long long t_wait, t_staged, t_computed;   // first unit of a phase (trace)
+    unsigned long long t_wait, t_staged, t_computed, t_reduced, t_epi;   // first unit of a phase (trace)
 };
 
 // Completion of a phase is counted in kSlots counters kSlotStride words
@@ -386,51 +386,81 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // RMS factors r = 1 / sqrt(sum / K + eps) of the input rows from its
-// per-block sums of squares.  Wave w takes positions w + 4 k; lane l adds
-// partials l, l + 64, ... in order, then wave_sum: a fixed order that
-// depends only on the number of partials.  Every load is issued before any
-// is used (from a valid address, selected afterwards: a conditional load
-// with an else value makes the compiler wait for it before the next one).
-struct RmsParts {
-    float v[2][kPartsPerLane];
-};
-
-__device__ __forceinline__ void rms_load(RmsParts &pv, const PhaseDesc &P, int round, int M) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-        const int m = wave + 4 * (2 * round + k);
-#pragma unroll
-        for (int j = 0; j < kPartsPerLane; j++) {
-            const int i = lane + 64 * j;
-            const bool ok = m < M && i < P.n_parts;
-            const float x = gld(P.in_parts + (ok ? m * P.n_parts + i : 0));
-            pv.v[k][j] = ok ? x : 0.0f;
-        }
+// per-block sums of squares.  rms_fetch copies the M x n_parts partials into
+// LDS with the loads' LDS transfer (no registers held), issued with the
+// input staging; after the barrier that ends staging, rms_store has wave w
+// take positions w + 4 k: lane l adds partials l, l + 64, ... in order, then
+// wave_sum.  A fixed order that depends only on the number of partials.
+__device__ __forceinline__ void rms_fetch(float *parts, const PhaseDesc &P, int M) {
+    const int lane = threadIdx.x & 63;
+    const int wave = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    const int total = M * P.n_parts;
+    for (int k = wave; 64 * k < total; k += 4) {
+        const int f = 64 * k + lane;
+        if (f < total)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(P.in_parts + f),
+                                             (__attribute__((address_space(3))) void *)(parts + 64 * k), 4, 0, 0);
     }
 }
 
-__device__ __forceinline__ void rms_store(const RmsParts &pv, const PhaseDesc &P, int round, int M, float *rs) {
+__device__ __forceinline__ void rms_store(const float *parts, const PhaseDesc &P, int M, float *rs) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-        const int m = wave + 4 * (2 * round + k);
-        if (m < M) {
-            float t = 0.0f;
-#pragma unroll
-            for (int j = 0; j < kPartsPerLane; j++) t += pv.v[k][j];
-            const float tot = wave_sum(t);
-            if (lane == 0) rs[m] = 1.0f / sqrtf(tot / static_cast<float>(P.K) + P.eps);
-        }
+    for (int m = wave; m < M; m += 4) {
+        float t = 0.0f;
+        for (int i = lane; i < P.n_parts; i += 64) t += parts[m * P.n_parts + i];
+        const float tot = wave_sum(t);
+        if (lane == 0) rs[m] = 1.0f / sqrtf(tot / static_cast<float>(P.K) + P.eps);
     }
+}
+
+// Reductions over the 32 lanes of a half-wave (every lane gets the result):
+// within each row of 16 by DPP, then the two rows by one lane exchange.
+__device__ __forceinline__ float half_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x128>(v));
+    return fmaxf(v, __shfl_xor(v, 16, 64));
+}
+__device__ __forceinline__ float half_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x124>(v);
+    v += dpp_f<0x128>(v);
+    return v + __shfl_xor(v, 16, 64);
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+// integer sum over each row of 16 lanes
+__device__ __forceinline__ int row_sum(int v) {
+    v += dpp_i<0xB1>(v);
+    v += dpp_i<0x4E>(v);
+    v += dpp_i<0x124>(v);
+    v += dpp_i<0x128>(v);
+    return v;
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+    const int lo = dpp_i<CTRL>(static_cast<int>(v & 0xFFFFFFFFull));
+    const int hi = dpp_i<CTRL>(static_cast<int>(v >> 32));
+    return (static_cast<unsigned long long>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+__device__ __forceinline__ unsigned long long half_max64(unsigned long long v) {
+    v = umax64(v, dpp_u64<0xB1>(v));
+    v = umax64(v, dpp_u64<0x4E>(v));
+    v = umax64(v, dpp_u64<0x124>(v));
+    v = umax64(v, dpp_u64<0x128>(v));
+    return umax64(v, __shfl_xor(v, 16, 64));
 }
 
 // Epilogue of a finished row tile (LDS ystage [n_w][M][kRows]): y outputs
 // of the matrices in [mat_lo, mat_hi), argmax candidates and the requantised
-// next activation.
+// next activation.  Half-wave h takes positions h, h + 8 (lane = row).
 template <int M>
-__device__ __forceinline__ void finish_tile(const PhaseDesc &P, const float *ystage, int64_t row0, int mat_lo, int mat_hi,
-                            bool do_ep, float g_row, Shared<M> &sh) {
+__device__ __forceinline__ void finish_tile(const PhaseDesc &P, const float *ystage, int64_t row0, int mat_lo,
+                                            int mat_hi, bool do_ep, float g_row, Shared<M> &sh) {
     const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), static_cast<int64_t>(P.N) - row0));
     for (int mat = mat_lo; mat < mat_hi; mat++) {
         float *y = P.y[mat];
@@ -440,19 +470,16 @@ __device__ __forceinline__ void finish_tile(const PhaseDesc &P, const float *yst
             if (r < rows_here) gst(y + static_cast<int64_t>(m) * P.N + row0 + r, ystage[(mat * M + m) * kRows + r]);
         }
     }
+    const int hw = threadIdx.x >> 5, l32 = threadIdx.x & 31;
     if (P.argmax) {
-        const int lane = threadIdx.x & 63;
-        for (int m = 0; m < M; m++) {
-            unsigned long long b = 0ull;
-            for (int r = threadIdx.x; r < rows_here; r += kThreads)
-                b = umax64(b, pack_argmax(ystage[m * kRows + r], static_cast<uint32_t>(row0 + r)));
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) b = umax64(b, __shfl_xor(b, o, 64));
-            if (lane == 0 && b) atomicMax(&sh.best[m], b);
+        for (int m = hw; m < M; m += kThreads / 32) {
+            const unsigned long long key =
+                l32 < rows_here ? pack_argmax(ystage[m * kRows + l32], static_cast<uint32_t>(row0 + l32)) : 0ull;
+            const unsigned long long b = half_max64(key);
+            if (l32 == 0 && b) atomicMax(&sh.best[m], b);
         }
     }
     if (do_ep && P.ep_mode != SV_EP_NONE && rows_here == kRows) {
-        const int hw = threadIdx.x >> 5, l32 = threadIdx.x & 31;
         const int64_t N = P.N;
         for (int m = hw; m < M; m += kThreads / 32) {
             float v;
@@ -460,21 +487,15 @@ __device__ __forceinline__ void finish_tile(const PhaseDesc &P, const float *yst
             else v = ystage[(P.ep_src * M + m) * kRows + l32];
             const int64_t grow = row0 + l32;
             const float vg = P.gamma ? v * g_row : v;
-            float am = fabsf(vg);
-#pragma unroll
-            for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 32));
+            const float am = half_max(fabsf(vg));
             const float dd = am / 127.0f;
             const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
             float rq = roundf(vg * id);
             rq = fminf(fmaxf(rq, -127.0f), 127.0f);
             const int qi = static_cast<int>(rq);
+            const int s = row_sum(qi);
+            const float sq = half_sum(v * v);
             st_dev(P.oq + m * N + grow, static_cast<int8_t>(qi));
-            int s = qi;
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 32);
-            float sq = v * v;
-#pragma unroll
-            for (int o = 16; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 32);
             const int64_t gb = grow >> 5;
             if ((l32 & 15) == 0) st_dev(P.os16 + m * (N >> 4) + 2 * gb + (l32 >> 4), s);
             if (l32 == 0) {
@@ -500,7 +521,8 @@ struct MG {
 // of rows row0 + 4 grp + p, p < 4.
 template <int QT, int M, int NM>
 __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart,
-                                         int CS, Shared<M> &sh, bool do_wait, unsigned *status, bool restage) {
+                                         float *parts, int CS, Shared<M> &sh, bool do_wait, unsigned *status,
+                                         bool restage) {
     constexpr int MGV = MG<M>::value;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 3, jl = lane & 7;
@@ -553,7 +575,11 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
     bool need_rs = false;
     if (do_wait) {
         if (P.wait && !wait_ready(P.wait, P.wait_target, status, sh.abort)) return false;
-        if (threadIdx.x == 0) sh.t_wait = __builtin_amdgcn_s_memrealtime();
+        if (threadIdx.x == 0) {
+            sh.t_wait = __builtin_amdgcn_s_memrealtime();
+            sh.t_reduced = 0ull;
+            sh.t_epi = 0ull;
+        }
         need_rs = true;
     }
     float acc[NM][kR][M];
@@ -570,7 +596,10 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
         // same one (then it is still in LDS)
         if (restage || M > MGV) {
             __syncthreads();
+            if (m0 == 0 && need_rs && P.in_parts) rms_fetch(parts, P, M);
             stage_act(act, P, m0, mg, s_begin, cs, CS);
+            // LDS transfers of this wave are complete once its loads are
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
         if (do_wait && m0 == 0 && threadIdx.x == 0) sh.t_staged = __builtin_amdgcn_s_memrealtime();
@@ -602,9 +631,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
     // The input's RMS factors (first unit of a phase) are formed now, with
     // the weight registers free: their loads are in flight during the
     // reduction below.
-    RmsParts pv;
     const bool rms = need_rs && P.in_parts;
-    if (rms) rms_load(pv, P, 0, M);
     // Lanes of a row group: fixed-order sum; waves: partials through LDS,
     // added in wave order.
 #pragma unroll
@@ -617,11 +644,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
                 if (jl == 0) wpart[((wave * NM + mm) * M + m) * kRows + grp * kR + p] = v;
             }
     if (rms) {
-        rms_store(pv, P, 0, M, sh.rscale);
-        if (M > 8) {
-            rms_load(pv, P, 1, M);
-            rms_store(pv, P, 1, M, sh.rscale);
-        }
+        rms_store(parts, P, M, sh.rscale);
     } else if (need_rs && threadIdx.x < M) {
         sh.rscale[threadIdx.x] = 1.0f;
     }
@@ -645,7 +668,9 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
     }
     if (!split) {
         __syncthreads();
+        if (do_wait && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
         finish_tile<M>(P, ystage, row0, mat, mat + NM, NM == 2 || mat == P.ep_src, g_row, sh);
+        if (do_wait && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
         return true;
     }
     // K split over units: the last unit of the tile to finish adds the chunk
@@ -680,21 +705,24 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
     if (threadIdx.x == 0)
         st_dev(P.tile_count + tile, 0u);
     __syncthreads();
+    if (do_wait && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
     finish_tile<M>(P, ystage, row0, 0, P.n_w, true, g_row, sh);
+    if (do_wait && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
     return true;
 }
 
 template <int M>
 __device__ __forceinline__ bool dispatch_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart,
-                                              int CS, Shared<M> &sh, bool do_wait, unsigned *status,
+                                              float *parts, int CS, Shared<M> &sh, bool do_wait, unsigned *status,
                                               bool restage = true) {
     if (P.qtype == SV_Q4_K) {
-        if (P.fused) return run_unit<SV_Q4_K, M, 2>(P, unit, act, ystage, wpart, CS, sh, do_wait, status, restage);
-        return run_unit<SV_Q4_K, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status, restage);
+        if (P.fused)
+            return run_unit<SV_Q4_K, M, 2>(P, unit, act, ystage, wpart, parts, CS, sh, do_wait, status, restage);
+        return run_unit<SV_Q4_K, M, 1>(P, unit, act, ystage, wpart, parts, CS, sh, do_wait, status, restage);
     }
     if (P.qtype == SV_Q6_K)
-        return run_unit<SV_Q6_K, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status, restage);
-    return run_unit<SV_Q8_0, M, 1>(P, unit, act, ystage, wpart, CS, sh, do_wait, status, restage);
+        return run_unit<SV_Q6_K, M, 1>(P, unit, act, ystage, wpart, parts, CS, sh, do_wait, status, restage);
+    return run_unit<SV_Q8_0, M, 1>(P, unit, act, ystage, wpart, parts, CS, sh, do_wait, status, restage);
 }
 
 __device__ __forceinline__ void flush_best(const PhaseDesc &P, unsigned long long *best, int M) {
@@ -707,11 +735,13 @@ __device__ __forceinline__ void flush_best(const PhaseDesc &P, unsigned long lon
 }
 
 // LDS layout of a workgroup: act chunk [MG][CS * kActRec] | ystage
-// [3][M][kRows] fp32 | wave partials [4][2][M][kRows] fp32.
+// [3][M][kRows] fp32 | wave partials [4][2][M][kRows] fp32 | the input's
+// sums of squares [M][n_parts] fp32.
 template <int M>
-__device__ __forceinline__ void lds_parts(uint8_t *smem, int CS, float *&ystage, float *&wpart) {
+__device__ __forceinline__ void lds_parts(uint8_t *smem, int CS, float *&ystage, float *&wpart, float *&parts) {
     ystage = reinterpret_cast<float *>(smem + MG<M>::value * CS * kActRec);
     wpart = ystage + 3 * M * kRows;
+    parts = wpart + 8 * M * kRows;
 }
 
 // One workgroup per unit of a single phase.
@@ -719,17 +749,18 @@ template <int M>
 __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void phase_kernel(PhaseDesc P, int CS) {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ Shared<M> sh;
-    float *ystage, *wpart;
-    lds_parts<M>(smem, CS, ystage, wpart);
+    float *ystage, *wpart, *parts;
+    lds_parts<M>(smem, CS, ystage, wpart, parts);
     if (threadIdx.x < SV_MAX_M) sh.best[threadIdx.x] = 0ull;
-    dispatch_unit<M>(P, blockIdx.x, smem, ystage, wpart, CS, sh, true, nullptr);
+    dispatch_unit<M>(P, blockIdx.x, smem, ystage, wpart, parts, CS, sh, true, nullptr);
     flush_best(P, sh.best, M);
 }
 
 // Trace record of a (workgroup, phase): real-time counter at phase entry,
 // input ready, input staged, first unit computed, first unit done, last
-// unit done; units run; unused.
-constexpr int kTraceWords = 8;
+// unit done; units run; first unit reduced (partials combined), first unit's
+// epilogue written; unused.
+constexpr int kTraceWords = 12;
 
 // ctl: [1] status, [2] exited workgroups, then per phase kSlots counters of
 // finished units.  The last workgroup to exit returns every counter but the
@@ -741,8 +772,8 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const Ph
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ Shared<M> sh;
     __shared__ PhaseDesc P;
-    float *ystage, *wpart;
-    lds_parts<M>(smem, CS, ystage, wpart);
+    float *ystage, *wpart, *parts;
+    lds_parts<M>(smem, CS, ystage, wpart, parts);
     unsigned *status = ctl + 1;
     if (threadIdx.x < SV_MAX_M) sh.best[threadIdx.x] = 0ull;
     // Workgroup 0 clears the head's argmax: no head tile can finish before
@@ -769,7 +800,8 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const Ph
         for (; u < nu; u += G) {
             const int chunk = static_cast<int>(u % P.per_tile) % P.S;
             const int c0 = static_cast<int>(static_cast<int64_t>(chunk) * P.steps / P.S);
-            ok = dispatch_unit<M>(P, static_cast<int>(u), smem, ystage, wpart, CS, sh, first, status, c0 != staged);
+            ok = dispatch_unit<M>(P, static_cast<int>(u), smem, ystage, wpart, parts, CS, sh, first, status,
+                                  c0 != staged);
             staged = c0;
             if (!ok) break;
             n_done++;
@@ -786,6 +818,8 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const Ph
                     tr[2] = sh.t_staged;
                     tr[3] = sh.t_computed;
                     tr[4] = __builtin_amdgcn_s_memrealtime();
+                    tr[7] = sh.t_reduced;
+                    tr[8] = sh.t_epi;
                 }
             }
             first = false;
@@ -857,10 +891,10 @@ static void decompose(PhaseDesc &P) {
     P.chunk_sub = ((P.steps + P.S - 1) / P.S) * 8;
 }
 
-static size_t lds_bytes(int M, int CS) {
+static size_t lds_bytes(int M, int CS, int NP) {
     const int mg = M > 8 ? 8 : M;
     return static_cast<size_t>(mg) * CS * kActRec + static_cast<size_t>(3) * M * kRows * 4 +
-           static_cast<size_t>(8) * M * kRows * 4;
+           static_cast<size_t>(8) * M * kRows * 4 + static_cast<size_t>(M) * NP * 4;
 }
 
 static bool needs_partials(const PhaseDesc &P) { return P.S > 1 || (P.ep_mode == SV_EP_PAIR && !P.fused); }
@@ -984,7 +1018,7 @@ static int launch_single(PhaseDesc &P, int M, void *ws, size_t ws_bytes, hipStre
         P.partial = reinterpret_cast<float *>(b + kCounterBytes);
     }
     const int CS = P.chunk_sub;
-    const size_t lds = lds_bytes(M, CS);
+    const size_t lds = lds_bytes(M, CS, P.n_parts);
     SV_REQUIRE(lds <= 64 * 1024, SV_ERR_SHAPE, "internal: LDS budget exceeded");
     launch_any(M, false, P, nullptr, 0, nullptr, P.n_units, CS, lds, st);
     return hip_check(hipGetLastError(), "projection launch");
@@ -1047,7 +1081,7 @@ extern "C" int sv_head_logits(const sv_weight *H, const sv_act *A, const int32_t
 
 // ------------------------------------------------------------ whole pass
 struct sv_pass {
-    int M, n_phases, grid, CS;
+    int M, n_phases, grid, CS, NP;
     uint32_t n_tickets;
     sv::PhaseDesc *table;        // device
     unsigned *ctl;               // device: status, exit count, completion slots
@@ -1158,9 +1192,13 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
                                         "256-byte blocks; every phase needs buffers of its own");
             }
     }
-    int chunk = 0;
-    for (auto &P : p->host) chunk = std::max(chunk, P.chunk_sub);
+    int chunk = 0, np = 0;
+    for (auto &P : p->host) {
+        chunk = std::max(chunk, P.chunk_sub);
+        np = std::max(np, P.n_parts);
+    }
     p->CS = chunk;
+    p->NP = np;
     int dev = 0;
     hipDeviceProp_t prop;
     int rc = hip_check(hipGetDevice(&dev), "pass_create");
@@ -1171,7 +1209,7 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
     }
     // Every workgroup of the pass must be resident at once (they wait on each
     // other's phases): the grid is what the GPU holds of this kernel.
-    const int occ = occupancy_any(p->M, lds_bytes(p->M, p->CS));
+    const int occ = occupancy_any(p->M, lds_bytes(p->M, p->CS, p->NP));
     if (occ < 1) {
         delete p;
         return fail(SV_ERR_HIP, "pass_create: could not query occupancy");
@@ -1196,7 +1234,7 @@ extern "C" int sv_pass_run(const sv_pass *p, void *stream) {
     using namespace sv;
     SV_REQUIRE(p, SV_ERR_ARG, "pass_run: NULL pass");
     hipStream_t st = as_stream(stream);
-    const size_t lds = lds_bytes(p->M, p->CS);
+    const size_t lds = lds_bytes(p->M, p->CS, p->NP);
     SV_REQUIRE(lds <= 64 * 1024, SV_ERR_SHAPE, "internal: LDS budget exceeded");
     launch_any(p->M, true, PhaseDesc{}, p->table, p->n_phases, p->ctl, p->grid, p->CS, lds, st, p->argmax,
                p->tracing ? p->trace : nullptr);
