@@ -246,6 +246,12 @@ struct Shared {
     unsigned long long t_wait, t_staged, t_computed, t_reduced, t_epi;   // first unit of a phase (trace)
 };
 
+// Workgroup barrier for LDS data only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a full __syncthreads
+// would also wait for weight records already requested for the next unit).
+// No global memory written before it is read by another wave after it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Completion of a phase is counted in kSlots counters kSlotStride words
 // apart (unit u adds to slot u % kSlots), so finishing units do not all
 // serialise on one address; a waiter sums the slots.
@@ -513,58 +519,96 @@ struct MG {
     static constexpr int value = M > 8 ? 8 : M;
 };
 
+// The rows, K chunk and matrix of a unit; wave w takes steps [w0, w1).
+struct UnitGeom {
+    int tile, chunk, mat, c0, w0, w1, cs;
+    int64_t row0, s_begin;
+};
+
+__device__ __forceinline__ UnitGeom unit_geom(const PhaseDesc &P, int unit) {
+    UnitGeom g;
+    const int wave = threadIdx.x >> 6;
+    g.tile = unit / P.per_tile;
+    const int rem = unit % P.per_tile;
+    g.chunk = rem % P.S;
+    g.mat = rem / P.S;
+    g.row0 = static_cast<int64_t>(g.tile) * kRows;
+    const int64_t nsub = P.K >> 5;
+    g.c0 = static_cast<int>(static_cast<int64_t>(g.chunk) * P.steps / P.S);
+    const int c1 = static_cast<int>(static_cast<int64_t>(g.chunk + 1) * P.steps / P.S);
+    const int tc = c1 - g.c0;
+    g.w0 = g.c0 + wave * tc / 4;
+    g.w1 = g.c0 + (wave + 1) * tc / 4;
+    g.s_begin = static_cast<int64_t>(g.c0) * 8;
+    g.cs = static_cast<int>(min(static_cast<int64_t>(tc) * 8, nsub - g.s_begin));
+    return g;
+}
+
+// Request every weight record of a unit (at most kMaxWaveSteps steps per
+// wave and matrix) into raw.
+// ALL: every record is written (steps a wave does not take re-read a
+// record of its chunk), so no value of an earlier unit has to be kept.
+template <int QT, int NM, bool ALL = false>
+__device__ __forceinline__ void issue_weights(WRaw<QT> (&raw)[NM][kMaxWaveSteps][kR], const PhaseDesc &P,
+                                              const UnitGeom &g) {
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 3, jl = lane & 7;
+    const int64_t nsub = P.K >> 5;
+    int64_t srow[kR];
+#pragma unroll
+    for (int p = 0; p < kR; p++) {
+        int64_t rr = g.row0 + grp * kR + p;
+        if (rr >= P.N) rr = 0;
+        const int64_t sr = P.row_ids ? static_cast<int64_t>(gld(P.row_ids + rr)) : rr;
+        // out-of-range ids are a caller error; clamp so no read leaves the matrix
+        srow[p] = (sr < 0 || sr >= P.wrows) ? 0 : sr;
+    }
+#pragma unroll
+    for (int mm = 0; mm < NM; mm++) {
+        const uint8_t *__restrict__ w = P.w[g.mat + mm];
+#pragma unroll
+        for (int t = 0; t < kMaxWaveSteps; t++) {
+            const int64_t sb = static_cast<int64_t>(g.w0 + t) * 8 + jl;
+            if (ALL) {
+                const int64_t sc = (g.w0 + t < g.w1 && sb < nsub) ? sb : static_cast<int64_t>(g.c0) * 8;
+#pragma unroll
+                for (int p = 0; p < kR; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sc);
+            } else if (g.w0 + t < g.w1 && sb < nsub) {
+#pragma unroll
+                for (int p = 0; p < kR; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sb);
+            }
+        }
+    }
+}
+
 // One unit: rows [row0, row0 + 32) x the K chunk `chunk`, for NM matrices
 // from `mat` (NM = 2: both matrices of a gate/up pair, so the pair's
 // product forms inside the unit).  Wave w takes steps [w0, w1) of the chunk
 // of each matrix (one step = 8 sub-blocks per row, one 256-element
 // super-block of a K-quant); lane j of row group grp reads sub-block 8 t + j
 // of rows row0 + 4 grp + p, p < 4.
-template <int QT, int M, int NM>
-__device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart,
-                                         float *parts, int CS, Shared<M> &sh, bool do_wait, unsigned *status,
-                                         bool restage) {
+// OWN: the unit requests its own weights first (raw is scratch); else raw
+// already holds them (software-pipelined phases) and next >= 0 names the
+// unit whose weights to request once the dot products are done.
+template <int QT, int M, int NM, bool OWN>
+__device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> (&raw_in)[NM][kMaxWaveSteps][kR],
+                                         int next, uint8_t *act, float *ystage, float *wpart, float *parts, int CS,
+                                         Shared<M> &sh, bool do_wait, unsigned *status, bool restage) {
     constexpr int MGV = MG<M>::value;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 3, jl = lane & 7;
     const bool pair = P.ep_mode == SV_EP_PAIR;
     const int per_tile = P.per_tile;
-    const int tile = unit / per_tile;
-    const int rem = unit % per_tile;
-    const int chunk = rem % P.S;
-    const int mat = rem / P.S;
-    const int64_t row0 = static_cast<int64_t>(tile) * kRows;
+    const UnitGeom g = unit_geom(P, unit);
+    const int tile = g.tile, chunk = g.chunk, mat = g.mat;
+    const int64_t row0 = g.row0;
     const int64_t nsub = P.K >> 5;
-    const int c0 = static_cast<int>(static_cast<int64_t>(chunk) * P.steps / P.S);
-    const int c1 = static_cast<int>(static_cast<int64_t>(chunk + 1) * P.steps / P.S);
-    const int tc = c1 - c0;
-    const int w0 = c0 + wave * tc / 4, w1 = c0 + (wave + 1) * tc / 4;
-    const int64_t s_begin = static_cast<int64_t>(c0) * 8;
-    const int cs = static_cast<int>(min(static_cast<int64_t>(tc) * 8, nsub - s_begin));
-
-    int64_t srow[kR];
-#pragma unroll
-    for (int p = 0; p < kR; p++) {
-        int64_t rr = row0 + grp * kR + p;
-        if (rr >= P.N) rr = 0;
-        const int64_t sr = P.row_ids ? static_cast<int64_t>(gld(P.row_ids + rr)) : rr;
-        // out-of-range ids are a caller error; clamp so no read leaves the matrix
-        srow[p] = (sr < 0 || sr >= P.wrows) ? 0 : sr;
-    }
-    // Every weight record of this unit is requested before waiting for the
-    // input (at most kMaxWaveSteps steps per wave and matrix).
-    WRaw<QT> raw[NM][kMaxWaveSteps][kR];
-#pragma unroll
-    for (int mm = 0; mm < NM; mm++) {
-        const uint8_t *__restrict__ w = P.w[mat + mm];
-#pragma unroll
-        for (int t = 0; t < kMaxWaveSteps; t++) {
-            const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
-            if (w0 + t < w1 && sb < nsub) {
-#pragma unroll
-                for (int p = 0; p < kR; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sb);
-            }
-        }
-    }
+    const int w0 = g.w0, w1 = g.w1;
+    const int64_t s_begin = g.s_begin;
+    const int cs = g.cs;
+    WRaw<QT> raw_own[NM][kMaxWaveSteps][kR];
+    WRaw<QT>(&raw)[NM][kMaxWaveSteps][kR] = OWN ? raw_own : raw_in;
+    if (OWN) issue_weights<QT, NM>(raw, P, g);
     // the epilogue's norm weight of this thread's row, fetched off the
     // critical path
     float g_row = 1.0f;
@@ -595,12 +639,12 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
         // the chunk staged for the previous unit of this phase may be the
         // same one (then it is still in LDS)
         if (restage || M > MGV) {
-            __syncthreads();
+            lds_barrier();
             if (m0 == 0 && need_rs && P.in_parts) rms_fetch(parts, P, M);
             stage_act(act, P, m0, mg, s_begin, cs, CS);
             // LDS transfers of this wave are complete once its loads are
             __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            lds_barrier();
         }
         if (do_wait && m0 == 0 && threadIdx.x == 0) sh.t_staged = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
@@ -628,6 +672,9 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
         }
     }
     if (do_wait && threadIdx.x == 0) sh.t_computed = __builtin_amdgcn_s_memrealtime();
+    // The weight registers are free: the next unit's records are requested
+    // now, so they stream in during this unit's reduction and epilogue.
+    if (!OWN && next >= 0) issue_weights<QT, NM, true>(raw, P, unit_geom(P, next));
     // The input's RMS factors (first unit of a phase) are formed now, with
     // the weight registers free: their loads are in flight during the
     // reduction below.
@@ -648,7 +695,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
     } else if (need_rs && threadIdx.x < M) {
         sh.rscale[threadIdx.x] = 1.0f;
     }
-    __syncthreads();
+    lds_barrier();
     // chunk value of (m, row) = ((w0 + w1) + w2) + w3.  A tile is final here
     // unless K is split over units or a pair's matrices sit in two units.
     const bool split = P.S > 1 || (pair && NM == 1);
@@ -667,7 +714,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
         }
     }
     if (!split) {
-        __syncthreads();
+        lds_barrier();
         if (do_wait && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
         finish_tile<M>(P, ystage, row0, mat, mat + NM, NM == 2 || mat == P.ep_src, g_row, sh);
         if (do_wait && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
@@ -681,7 +728,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
         const unsigned prev = add_dev(P.tile_count + tile, 1u);
         sh.last = (prev == static_cast<unsigned>(per_tile - 1)) ? 1 : 0;
     }
-    __syncthreads();
+    lds_barrier();
     if (!sh.last) return true;
     const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), static_cast<int64_t>(P.N) - row0));
     for (int i = threadIdx.x; i < P.n_w * M * kRows; i += kThreads) {
@@ -704,25 +751,90 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, uint8_t *
     }
     if (threadIdx.x == 0)
         st_dev(P.tile_count + tile, 0u);
-    __syncthreads();
+    lds_barrier();
     if (do_wait && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
     finish_tile<M>(P, ystage, row0, 0, P.n_w, true, g_row, sh);
     if (do_wait && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
     return true;
 }
 
+// Trace record of a (workgroup, phase): real-time counter at phase entry,
+// input ready, input staged, first unit computed, first unit done, last
+// unit done; units run; first unit reduced (partials combined), first unit's
+// epilogue written; unused.
+constexpr int kTraceWords = 12;
+
+// The units u, u + G, ... < nu of one phase on this workgroup.  A unit whose
+// output the next phase reads is drained and counted; any other unit lets
+// the next one's weights stream in during its own reduction and epilogue.
+template <int QT, int M, int NM, bool PF>
+__device__ __forceinline__ bool run_phase(const PhaseDesc &P, uint32_t u, uint32_t G, uint32_t nu, uint8_t *act,
+                                          float *ystage, float *wpart, float *parts, int CS, Shared<M> &sh,
+                                          unsigned *status, unsigned long long *tr) {
+    WRaw<QT> raw[NM][kMaxWaveSteps][kR];
+    if (PF) issue_weights<QT, NM, true>(raw, P, unit_geom(P, static_cast<int>(u)));
+    bool first = true;
+    int staged = -1;   // first step of the K chunk in LDS
+    unsigned n_done = 0;
+    for (; u < nu; u += G) {
+        const int rem = static_cast<int>(u % P.per_tile);
+        const int chunk = rem % P.S;
+        const int c0 = static_cast<int>(static_cast<int64_t>(chunk) * P.steps / P.S);
+        // Only units whose outputs the next phase reads are handed off
+        // (drained and counted); the last phase has no reader at all.
+        const bool counted = P.ready && (P.count_all || rem / P.S == P.ep_src);
+        const bool more = u + G < nu;
+        const int next = (PF && more && !counted) ? static_cast<int>(u + G) : -1;
+        if (!run_unit<QT, M, NM, !PF>(P, static_cast<int>(u), raw, next, act, ystage, wpart, parts, CS, sh, first,
+                                      status, c0 != staged))
+            return false;
+        staged = c0;
+        n_done++;
+        if (counted) drain();
+        lds_barrier();
+        if (threadIdx.x == 0) {
+            if (counted) add_dev(P.ready + (u % kSlots) * kSlotStride, 1u);
+            sh.last = 0;
+            if (first && tr) {
+                tr[1] = sh.t_wait;
+                tr[2] = sh.t_staged;
+                tr[3] = sh.t_computed;
+                tr[4] = __builtin_amdgcn_s_memrealtime();
+                tr[7] = sh.t_reduced;
+                tr[8] = sh.t_epi;
+            }
+        }
+        first = false;
+        lds_barrier();
+        if (PF && more && next < 0) issue_weights<QT, NM, true>(raw, P, unit_geom(P, static_cast<int>(u + G)));
+    }
+    if (tr && threadIdx.x == 0) {
+        tr[5] = __builtin_amdgcn_s_memrealtime();
+        tr[6] = n_done;
+    }
+    return true;
+}
+
 template <int M>
-__device__ __forceinline__ bool dispatch_unit(const PhaseDesc &P, int unit, uint8_t *act, float *ystage, float *wpart,
-                                              float *parts, int CS, Shared<M> &sh, bool do_wait, unsigned *status,
-                                              bool restage = true) {
+__device__ __forceinline__ bool dispatch_phase(const PhaseDesc &P, uint32_t u, uint32_t G, uint32_t nu, uint8_t *act,
+                                               float *ystage, float *wpart, float *parts, int CS, Shared<M> &sh,
+                                               unsigned *status, unsigned long long *tr) {
+    // Phases with several units per workgroup and no reader (the head) run
+    // software-pipelined: each unit's successor streams in during its
+    // reduction and epilogue.
+    if (!P.ready && u + G < nu) {
+        if (P.qtype == SV_Q6_K)
+            return run_phase<SV_Q6_K, M, 1, true>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
+        if (P.qtype == SV_Q8_0)
+            return run_phase<SV_Q8_0, M, 1, true>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
+    }
     if (P.qtype == SV_Q4_K) {
-        if (P.fused)
-            return run_unit<SV_Q4_K, M, 2>(P, unit, act, ystage, wpart, parts, CS, sh, do_wait, status, restage);
-        return run_unit<SV_Q4_K, M, 1>(P, unit, act, ystage, wpart, parts, CS, sh, do_wait, status, restage);
+        if (P.fused) return run_phase<SV_Q4_K, M, 2, false>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
+        return run_phase<SV_Q4_K, M, 1, false>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
     }
     if (P.qtype == SV_Q6_K)
-        return run_unit<SV_Q6_K, M, 1>(P, unit, act, ystage, wpart, parts, CS, sh, do_wait, status, restage);
-    return run_unit<SV_Q8_0, M, 1>(P, unit, act, ystage, wpart, parts, CS, sh, do_wait, status, restage);
+        return run_phase<SV_Q6_K, M, 1, false>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
+    return run_phase<SV_Q8_0, M, 1, false>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
 }
 
 __device__ __forceinline__ void flush_best(const PhaseDesc &P, unsigned long long *best, int M) {
@@ -752,15 +864,10 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void phase_kernel(PhaseDe
     float *ystage, *wpart, *parts;
     lds_parts<M>(smem, CS, ystage, wpart, parts);
     if (threadIdx.x < SV_MAX_M) sh.best[threadIdx.x] = 0ull;
-    dispatch_unit<M>(P, blockIdx.x, smem, ystage, wpart, parts, CS, sh, true, nullptr);
+    dispatch_phase<M>(P, blockIdx.x, gridDim.x, static_cast<uint32_t>(P.n_units), smem, ystage, wpart, parts, CS, sh,
+                      nullptr, nullptr);
     flush_best(P, sh.best, M);
 }
-
-// Trace record of a (workgroup, phase): real-time counter at phase entry,
-// input ready, input staged, first unit computed, first unit done, last
-// unit done; units run; first unit reduced (partials combined), first unit's
-// epilogue written; unused.
-constexpr int kTraceWords = 12;
 
 // ctl: [1] status, [2] exited workgroups, then per phase kSlots counters of
 // finished units.  The last workgroup to exit returns every counter but the
@@ -792,43 +899,9 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const Ph
         if (threadIdx.x == 0) P = table[p];
         __syncthreads();
         cur = p;
-        bool first = true;
         unsigned long long *tr = trace ? trace + (static_cast<size_t>(b) * n_phases + p) * kTraceWords : nullptr;
         if (tr && threadIdx.x == 0) tr[0] = __builtin_amdgcn_s_memrealtime();
-        unsigned n_done = 0;
-        int staged = -1;   // first step of the K chunk in LDS (this phase)
-        for (; u < nu; u += G) {
-            const int chunk = static_cast<int>(u % P.per_tile) % P.S;
-            const int c0 = static_cast<int>(static_cast<int64_t>(chunk) * P.steps / P.S);
-            ok = dispatch_unit<M>(P, static_cast<int>(u), smem, ystage, wpart, parts, CS, sh, first, status,
-                                  c0 != staged);
-            staged = c0;
-            if (!ok) break;
-            n_done++;
-            // Only units whose outputs the next phase reads are handed off
-            // (drained and counted); the last phase has no reader at all.
-            const bool counted = P.ready && (P.count_all || static_cast<int>((u % P.per_tile) / P.S) == P.ep_src);
-            if (counted) drain();
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                if (counted) add_dev(P.ready + (u % kSlots) * kSlotStride, 1u);
-                sh.last = 0;
-                if (first && tr) {
-                    tr[1] = sh.t_wait;
-                    tr[2] = sh.t_staged;
-                    tr[3] = sh.t_computed;
-                    tr[4] = __builtin_amdgcn_s_memrealtime();
-                    tr[7] = sh.t_reduced;
-                    tr[8] = sh.t_epi;
-                }
-            }
-            first = false;
-            __syncthreads();
-        }
-        if (tr && threadIdx.x == 0) {
-            tr[5] = __builtin_amdgcn_s_memrealtime();
-            tr[6] = n_done;
-        }
+        ok = dispatch_phase<M>(P, u, G, nu, smem, ystage, wpart, parts, CS, sh, status, tr);
     }
     if (cur >= 0) flush_best(P, sh.best, M);
     drain();
