@@ -191,23 +191,38 @@ __device__ __forceinline__ void decode_w(WDec &o, const WRaw<QT> &r, int j8) {
 struct ARec {
     uint32_t v[8];
     float d;
-    float xf;        // Q4_K: fp32 sum of the 32 codes
-    int32_t x0, x1;  // Q6_K: -32 * (sum of codes of each 16-element half)
+    int32_t x0, x1;  // exact sums of the codes of each 16-element half
 };
 
-// One block term for one (row slot, position), accumulated into acc.
+// Per-position terms of a sub-block shared by the four row slots of a lane:
+// Q4_K's fp32 code sum (min term), Q6_K's -32 offset of each half as the
+// starting value of that half's integer dot product.
+struct AExt {
+    float xf;
+    int32_t o0, o1;
+};
 template <int QT>
-__device__ __forceinline__ float block_term(const WDec &w, const ARec &a, float acc) {
+__device__ __forceinline__ AExt act_ext(const ARec &a) {
+    AExt e;
+    e.xf = static_cast<float>(a.x0 + a.x1);
+    e.o0 = -32 * a.x0;
+    e.o1 = -32 * a.x1;
+    return e;
+}
+
+// One block term for one (row slot, position), accumulated into acc.  All
+// integer parts are exact, so the value does not depend on how they are
+// grouped: Q6_K's sum over (q - 32) a of each half is the dot product of the
+// stored 6-bit codes started at -32 * (sum of a).
+template <int QT>
+__device__ __forceinline__ float block_term(const WDec &w, const ARec &a, const AExt &e, float acc) {
     if constexpr (QT == SV_Q6_K) {
-        int32_t S0 = 0, S1 = 0;
+        int32_t S0 = e.o0, S1 = e.o1;
 #pragma unroll
         for (int k = 0; k < 4; k++) S0 = dot4(w.v[k], a.v[k], S0);
 #pragma unroll
         for (int k = 4; k < 8; k++) S1 = dot4(w.v[k], a.v[k], S1);
-        int32_t I = __mul24(w.i0, S0);
-        I += __mul24(w.i1, S1);
-        I += __mul24(w.i0, a.x0);
-        I += __mul24(w.i1, a.x1);
+        const int32_t I = __mul24(w.i0, S0) + __mul24(w.i1, S1);
         return fmaf(w.s0 * a.d, static_cast<float>(I), acc);
     } else {
         int32_t S = 0;
@@ -216,7 +231,7 @@ __device__ __forceinline__ float block_term(const WDec &w, const ARec &a, float 
         if constexpr (QT == SV_Q8_0) {
             return fmaf(w.s0 * a.d, static_cast<float>(S), acc);
         } else {
-            const float inner = fmaf(-w.s1, a.xf, w.s0 * static_cast<float>(S));
+            const float inner = fmaf(-w.s1, e.xf, w.s0 * static_cast<float>(S));
             return fmaf(a.d, inner, acc);
         }
     }
@@ -233,7 +248,6 @@ __device__ __forceinline__ void read_act(ARec &r, const uint8_t *act_m, int CS, 
     const int2 x = reinterpret_cast<const int2 *>(act_m + CS * 36)[sl];
     r.x0 = x.x;
     r.x1 = x.y;
-    r.xf = __int_as_float(x.x);
 }
 
 // Shared state of a workgroup.
@@ -293,74 +307,72 @@ __device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target,
     return abort_sh == 0u;
 }
 
+constexpr int kPartsPerLane = 9;  // >= 544 partials / 64 lanes
+
 // Stage positions [m0, m0 + mg) of the chunk's sub-blocks [s0, s0 + cs) into
-// LDS and, when rs is given, form the input's RMS factors in the same round
-// trip (lane-strided sequential sums over the partials, then a butterfly
-// over the wave: a fixed order that depends only on n_parts).  Every global
-// load of a thread is issued before the first one is used.
+// LDS.  Thread t takes items t, t + 256, ... of the 16-byte halves and of the
+// (scale, sums) records; every global load of a thread is issued before the
+// first one is stored.  The item index i splits into (position, offset) as
+// i / D = (i * ceil(2^20 / D)) >> 20, exact for i < 2^11 and D <= 512 (the
+// rounding error i / 2^20 stays below 1 / D), so no lane divides.
 constexpr int kStageHalf = 6;   // >= 8 positions * 96 sub-blocks * 2 halves / 256 threads
 constexpr int kStageRec = 3;    // >= 8 * 96 / 256
-constexpr int kPartsPerLane = 9;  // >= 544 partials / 64 lanes
 
 __device__ __forceinline__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int64_t s0, int cs,
                                           int CS) {
     const int64_t K = P.K, nsub = K >> 5;
     const int nhalf = mg * cs * 2, nrec = mg * cs;
+    const uint32_t D2 = 2u * static_cast<uint32_t>(cs), D1 = static_cast<uint32_t>(cs);
+    const uint32_t mul2 = ((1u << 20) + D2 - 1) / D2, mul1 = ((1u << 20) + D1 - 1) / D1;
     // named registers, not arrays: a private array here ends up in scratch
     uint4 h0, h1, h2, h3, h4, h5;
-#define SV_LDH(k, hv)                                                                                   \
-    {                                                                                                   \
-        const int i = threadIdx.x + (k) * kThreads;                                                     \
-        if (i < nhalf) {                                                                                \
-            const int m = i / (cs * 2), r = i % (cs * 2), sl = r >> 1, h = r & 1;                        \
-            hv = gld16(P.aq + (m0 + m) * K + (s0 + sl) * 32 + h * 16);                                    \
-        }                                                                                               \
+#define SV_HALF(k)                                                                                       \
+    const int i = threadIdx.x + (k) * kThreads;                                                          \
+    const int m = static_cast<int>(__umul24(static_cast<uint32_t>(i), mul2) >> 20);                      \
+    const int r = i - m * static_cast<int>(D2), sl = r >> 1, h = r & 1;
+#define SV_LDH(k, hv)                                                                                    \
+    {                                                                                                    \
+        SV_HALF(k)                                                                                       \
+        if (i < nhalf) hv = gld16(P.aq + (m0 + m) * K + (s0 + sl) * 32 + h * 16);                         \
     }
     SV_LDH(0, h0) SV_LDH(1, h1) SV_LDH(2, h2) SV_LDH(3, h3) SV_LDH(4, h4) SV_LDH(5, h5)
 #undef SV_LDH
     float d0, d1, d2;
     uint2 x0, x1, x2;
-#define SV_LDR(k, dv, xv)                                                                               \
-    {                                                                                                   \
-        const int i = threadIdx.x + (k) * kThreads;                                                     \
-        if (i < nrec) {                                                                                 \
-            const int m = i / cs, sl = i % cs;                                                          \
-            dv = gld(P.ad + (m0 + m) * nsub + s0 + sl);                                                 \
-            xv = gld8(P.as16 + (m0 + m) * (K >> 4) + 2 * (s0 + sl));                                    \
-        }                                                                                               \
+#define SV_REC(k)                                                                                        \
+    const int i = threadIdx.x + (k) * kThreads;                                                          \
+    const int m = static_cast<int>(__umul24(static_cast<uint32_t>(i), mul1) >> 20);                      \
+    const int sl = i - m * static_cast<int>(D1);
+#define SV_LDR(k, dv, xv)                                                                                \
+    {                                                                                                    \
+        SV_REC(k)                                                                                        \
+        if (i < nrec) {                                                                                  \
+            dv = gld(P.ad + (m0 + m) * nsub + s0 + sl);                                                  \
+            xv = gld8(P.as16 + (m0 + m) * (K >> 4) + 2 * (s0 + sl));                                     \
+        }                                                                                                \
     }
     SV_LDR(0, d0, x0) SV_LDR(1, d1, x1) SV_LDR(2, d2, x2)
 #undef SV_LDR
-#define SV_STH(k, hv)                                                                                   \
-    {                                                                                                   \
-        const int i = threadIdx.x + (k) * kThreads;                                                     \
-        if (i < nhalf) {                                                                                \
-            const int m = i / (cs * 2), r = i % (cs * 2), sl = r >> 1, h = r & 1;                        \
-            *reinterpret_cast<uint4 *>(act + m * CS * kActRec + h * CS * 16 + sl * 16) = hv;              \
-        }                                                                                               \
+#define SV_STH(k, hv)                                                                                    \
+    {                                                                                                    \
+        SV_HALF(k)                                                                                       \
+        if (i < nhalf) *reinterpret_cast<uint4 *>(act + m * CS * kActRec + h * CS * 16 + sl * 16) = hv;    \
     }
     SV_STH(0, h0) SV_STH(1, h1) SV_STH(2, h2) SV_STH(3, h3) SV_STH(4, h4) SV_STH(5, h5)
 #undef SV_STH
-#define SV_STR(k, dv, xv)                                                                               \
-    {                                                                                                   \
-        const int i = threadIdx.x + (k) * kThreads;                                                     \
-        if (i < nrec) {                                                                                 \
-            const int m = i / cs, sl = i % cs;                                                          \
-            uint8_t *am = act + m * CS * kActRec;                                                       \
-            reinterpret_cast<float *>(am + CS * 32)[sl] = dv;                                           \
-            int2 x;                                                                                     \
-            if (P.qtype == SV_Q4_K) {                                                                   \
-                x.x = __float_as_int(static_cast<float>(static_cast<int32_t>(xv.x + xv.y)));            \
-                x.y = 0;                                                                                \
-            } else {                                                                                    \
-                x.x = -32 * static_cast<int32_t>(xv.x);                                                 \
-                x.y = -32 * static_cast<int32_t>(xv.y);                                                 \
-            }                                                                                           \
-            reinterpret_cast<int2 *>(am + CS * 36)[sl] = x;                                             \
-        }                                                                                               \
+#define SV_STR(k, dv, xv)                                                                                \
+    {                                                                                                    \
+        SV_REC(k)                                                                                        \
+        if (i < nrec) {                                                                                  \
+            uint8_t *am = act + m * CS * kActRec;                                                        \
+            reinterpret_cast<float *>(am + CS * 32)[sl] = dv;                                            \
+            reinterpret_cast<uint2 *>(am + CS * 36)[sl] = xv;                                            \
+        }                                                                                                \
     }
     SV_STR(0, d0, x0) SV_STR(1, d1, x1) SV_STR(2, d2, x2)
 #undef SV_STR
+#undef SV_HALF
+#undef SV_REC
 }
 
 // Sums over lanes with data-parallel primitives (no LDS traffic), in a fixed
@@ -593,7 +605,7 @@ __device__ __forceinline__ void issue_weights(WRaw<QT> (&raw)[NM][kMaxWaveSteps]
 template <int QT, int M, int NM, bool OWN>
 __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> (&raw_in)[NM][kMaxWaveSteps][kR],
                                          int next, uint8_t *act, float *ystage, float *wpart, float *parts, int CS,
-                                         Shared<M> &sh, bool do_wait, unsigned *status, bool restage) {
+                                         Shared<M> &sh, bool do_wait, bool timed, unsigned *status, bool restage) {
     constexpr int MGV = MG<M>::value;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 3, jl = lane & 7;
@@ -619,7 +631,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
     bool need_rs = false;
     if (do_wait) {
         if (P.wait && !wait_ready(P.wait, P.wait_target, status, sh.abort)) return false;
-        if (threadIdx.x == 0) {
+        if (timed && threadIdx.x == 0) {
             sh.t_wait = __builtin_amdgcn_s_memrealtime();
             sh.t_reduced = 0ull;
             sh.t_epi = 0ull;
@@ -646,7 +658,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
             __builtin_amdgcn_s_waitcnt(0);
             lds_barrier();
         }
-        if (do_wait && m0 == 0 && threadIdx.x == 0) sh.t_staged = __builtin_amdgcn_s_memrealtime();
+        if (timed && m0 == 0 && threadIdx.x == 0) sh.t_staged = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
         for (int t = 0; t < kMaxWaveSteps; t++) {
             const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
@@ -662,16 +674,17 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
                         if (m0 + m < M) {
                             ARec ar;
                             read_act(ar, act + m * CS * kActRec, CS, sl);
+                            const AExt ae = act_ext<QT>(ar);
 #pragma unroll
                             for (int p = 0; p < kR; p++)
-                                acc[mm][p][m0 + m] = block_term<QT>(dec[p], ar, acc[mm][p][m0 + m]);
+                                acc[mm][p][m0 + m] = block_term<QT>(dec[p], ar, ae, acc[mm][p][m0 + m]);
                         }
                     }
                 }
             }
         }
     }
-    if (do_wait && threadIdx.x == 0) sh.t_computed = __builtin_amdgcn_s_memrealtime();
+    if (timed && threadIdx.x == 0) sh.t_computed = __builtin_amdgcn_s_memrealtime();
     // The weight registers are free: the next unit's records are requested
     // now, so they stream in during this unit's reduction and epilogue.
     if (!OWN && next >= 0) issue_weights<QT, NM, true>(raw, P, unit_geom(P, next));
@@ -715,9 +728,9 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
     }
     if (!split) {
         lds_barrier();
-        if (do_wait && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
+        if (timed && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
         finish_tile<M>(P, ystage, row0, mat, mat + NM, NM == 2 || mat == P.ep_src, g_row, sh);
-        if (do_wait && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
+        if (timed && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
         return true;
     }
     // K split over units: the last unit of the tile to finish adds the chunk
@@ -752,9 +765,9 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
     if (threadIdx.x == 0)
         st_dev(P.tile_count + tile, 0u);
     lds_barrier();
-    if (do_wait && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
+    if (timed && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
     finish_tile<M>(P, ystage, row0, 0, P.n_w, true, g_row, sh);
-    if (do_wait && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
+    if (timed && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
     return true;
 }
 
@@ -786,7 +799,7 @@ __device__ __forceinline__ bool run_phase(const PhaseDesc &P, uint32_t u, uint32
         const bool more = u + G < nu;
         const int next = (PF && more && !counted) ? static_cast<int>(u + G) : -1;
         if (!run_unit<QT, M, NM, !PF>(P, static_cast<int>(u), raw, next, act, ystage, wpart, parts, CS, sh, first,
-                                      status, c0 != staged))
+                                      first && tr != nullptr, status, c0 != staged))
             return false;
         staged = c0;
         n_done++;
