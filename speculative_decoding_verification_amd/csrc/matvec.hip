@@ -12,19 +12,20 @@
 // cut into units = (32-row tile, K chunk, matrix):
 //  * K is walked in steps of 256 elements (one K-quant super-block, eight
 //    Q8_0 blocks); a chunk is at most 12 steps, so S(K) = ceil(steps / 12)
-//    depends on K alone.  Each of the four waves takes <= 3 of the chunk's
-//    steps.
-//  * Lane j of an 8-lane row group reads sub-block 8t + j of four rows: the
+//    depends on K alone.  Wave w takes the 16-row half tile w & 1 over the
+//    half w >> 1 of the chunk's steps, so all four waves carry the same
+//    rows x steps.
+//  * Lane j of an 8-lane row group reads sub-block 8t + j of two rows: the
 //    group reads 128 contiguous bytes of a row, and each weight record is
 //    read once and reused from registers for all M positions.  The input
 //    chunk is staged in LDS once per unit.
 // Arithmetic.  Integer block sums come from v_dot4 (exact); each block's
 // fp32 combine is a fixed sequence of operations per (row, position); a lane
 // adds its blocks in increasing order, the 8 lanes of a group are combined
-// by a butterfly, the four waves in wave order and the K chunks in chunk
-// order.  Nothing depends on M or on which workgroup ran which unit, so every
-// output row is bit-identical to the same row computed alone, and runs are
-// deterministic.
+// in a fixed DPP tree, the step parts in order and the K chunks in chunk
+// order.  Nothing depends on M or on which workgroup ran which unit,
+// so every output row is bit-identical to the same row computed alone, and
+// runs are deterministic.
 // Scheduling.  Single calls launch one workgroup per unit.  A whole pass
 // runs as one persistent launch sized to the number of workgroups the GPU
 // holds at once: the units of each phase are dealt round-robin, and a
@@ -38,14 +39,26 @@
 namespace sv {
 
 constexpr int kThreads = 256;          // four waves
-constexpr int kR = 4;                  // rows per lane
 constexpr int kRows = 32;              // rows per tile: 8 groups of 8 lanes x 4 rows
 constexpr int kActRec = 32 + 4 + 8;     // LDS bytes per position per staged sub-block
 constexpr int kMaxChunkSteps = 12;      // most 256-element steps of K one unit covers
-constexpr int kMaxWaveSteps = 3;        // = kMaxChunkSteps / 4 waves
 constexpr int kMaxS = 8;                // most K chunks (K <= 24576)
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kMaxGrid = 1024;          // most workgroups a pass launches
+
+// Lane layout of a unit: R rows per lane; the tile's rows are cut into
+// RS = 4 / R parts and the chunk's steps into SS = 4 / RS parts, wave w
+// taking row part w % RS over step part w / RS (at most WS steps).  Two rows
+// per lane give every wave the same rows x steps (a chunk's step count is
+// rarely a multiple of four).  The layout fixes the order of the fp32 sums,
+// so it must not depend on M: each position's result is bitwise the same at
+// every M.
+struct Lay {
+    static constexpr int R = 2;
+    static constexpr int RS = 4 / R;
+    static constexpr int SS = 4 / RS;
+    static constexpr int WS = kMaxChunkSteps / SS;
+};
 
 // Device-side description of one phase.
 struct PhaseDesc {
@@ -531,13 +544,17 @@ struct MG {
     static constexpr int value = M > 8 ? 8 : M;
 };
 
-// The rows, K chunk and matrix of a unit; wave w takes steps [w0, w1).
+// The rows, K chunk and matrix of a unit under the R-rows-per-lane layout:
+// wave w takes rows [rw, rw + 32 / RS), rw = row0 + (32 / RS) (w % RS),
+// over steps [w0, w1), the (w / RS)-th of SS parts of the chunk's steps.
 struct UnitGeom {
     int tile, chunk, mat, c0, w0, w1, cs;
-    int64_t row0, s_begin;
+    int64_t row0, rw, s_begin;
 };
 
+template <int R>
 __device__ __forceinline__ UnitGeom unit_geom(const PhaseDesc &P, int unit) {
+    constexpr int RS = 4 / R, SS = 4 / RS;
     UnitGeom g;
     const int wave = threadIdx.x >> 6;
     g.tile = unit / P.per_tile;
@@ -549,27 +566,28 @@ __device__ __forceinline__ UnitGeom unit_geom(const PhaseDesc &P, int unit) {
     g.c0 = static_cast<int>(static_cast<int64_t>(g.chunk) * P.steps / P.S);
     const int c1 = static_cast<int>(static_cast<int64_t>(g.chunk + 1) * P.steps / P.S);
     const int tc = c1 - g.c0;
-    g.w0 = g.c0 + wave * tc / 4;
-    g.w1 = g.c0 + (wave + 1) * tc / 4;
+    g.w0 = g.c0 + (wave / RS) * tc / SS;
+    g.w1 = g.c0 + (wave / RS + 1) * tc / SS;
+    g.rw = g.row0 + (kRows / RS) * (wave % RS);
     g.s_begin = static_cast<int64_t>(g.c0) * 8;
     g.cs = static_cast<int>(min(static_cast<int64_t>(tc) * 8, nsub - g.s_begin));
     return g;
 }
 
-// Request every weight record of a unit (at most kMaxWaveSteps steps per
+// Request every weight record of a unit (at most WS steps per
 // wave and matrix) into raw.
 // ALL: every record is written (steps a wave does not take re-read a
 // record of its chunk), so no value of an earlier unit has to be kept.
-template <int QT, int NM, bool ALL = false>
-__device__ __forceinline__ void issue_weights(WRaw<QT> (&raw)[NM][kMaxWaveSteps][kR], const PhaseDesc &P,
+template <int QT, int NM, bool ALL = false, int WS, int R>
+__device__ __forceinline__ void issue_weights(WRaw<QT> (&raw)[NM][WS][R], const PhaseDesc &P,
                                               const UnitGeom &g) {
     const int lane = threadIdx.x & 63;
     const int grp = lane >> 3, jl = lane & 7;
     const int64_t nsub = P.K >> 5;
-    int64_t srow[kR];
+    int64_t srow[R];
 #pragma unroll
-    for (int p = 0; p < kR; p++) {
-        int64_t rr = g.row0 + grp * kR + p;
+    for (int p = 0; p < R; p++) {
+        int64_t rr = g.rw + grp * R + p;
         if (rr >= P.N) rr = 0;
         const int64_t sr = P.row_ids ? static_cast<int64_t>(gld(P.row_ids + rr)) : rr;
         // out-of-range ids are a caller error; clamp so no read leaves the matrix
@@ -579,15 +597,15 @@ __device__ __forceinline__ void issue_weights(WRaw<QT> (&raw)[NM][kMaxWaveSteps]
     for (int mm = 0; mm < NM; mm++) {
         const uint8_t *__restrict__ w = P.w[g.mat + mm];
 #pragma unroll
-        for (int t = 0; t < kMaxWaveSteps; t++) {
+        for (int t = 0; t < WS; t++) {
             const int64_t sb = static_cast<int64_t>(g.w0 + t) * 8 + jl;
             if (ALL) {
                 const int64_t sc = (g.w0 + t < g.w1 && sb < nsub) ? sb : static_cast<int64_t>(g.c0) * 8;
 #pragma unroll
-                for (int p = 0; p < kR; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sc);
+                for (int p = 0; p < R; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sc);
             } else if (g.w0 + t < g.w1 && sb < nsub) {
 #pragma unroll
-                for (int p = 0; p < kR; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sb);
+                for (int p = 0; p < R; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sb);
             }
         }
     }
@@ -595,15 +613,16 @@ __device__ __forceinline__ void issue_weights(WRaw<QT> (&raw)[NM][kMaxWaveSteps]
 
 // One unit: rows [row0, row0 + 32) x the K chunk `chunk`, for NM matrices
 // from `mat` (NM = 2: both matrices of a gate/up pair, so the pair's
-// product forms inside the unit).  Wave w takes steps [w0, w1) of the chunk
-// of each matrix (one step = 8 sub-blocks per row, one 256-element
-// super-block of a K-quant); lane j of row group grp reads sub-block 8 t + j
-// of rows row0 + 4 grp + p, p < 4.
+// product forms inside the unit).  Wave w takes rows [rw, rw + 32 / RS)
+// over steps [w0, w1) of the chunk of each matrix (one step = 8 sub-blocks
+// per row, one 256-element super-block of a K-quant); lane j of row group
+// grp reads sub-block 8 t + j of rows rw + R grp + p, p < R.
 // OWN: the unit requests its own weights first (raw is scratch); else raw
 // already holds them (software-pipelined phases) and next >= 0 names the
 // unit whose weights to request once the dot products are done.
 template <int QT, int M, int NM, bool OWN>
-__device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> (&raw_in)[NM][kMaxWaveSteps][kR],
+__device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit,
+                                         WRaw<QT> (&raw_in)[NM][Lay::WS][Lay::R],
                                          int next, uint8_t *act, float *ystage, float *wpart, float *parts, int CS,
                                          Shared<M> &sh, bool do_wait, bool timed, unsigned *status, bool restage) {
     constexpr int MGV = MG<M>::value;
@@ -611,15 +630,16 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
     const int grp = lane >> 3, jl = lane & 7;
     const bool pair = P.ep_mode == SV_EP_PAIR;
     const int per_tile = P.per_tile;
-    const UnitGeom g = unit_geom(P, unit);
+    constexpr int kR = Lay::R, RS = Lay::RS, SS = Lay::SS, WS = Lay::WS;
+    const UnitGeom g = unit_geom<kR>(P, unit);
     const int tile = g.tile, chunk = g.chunk, mat = g.mat;
     const int64_t row0 = g.row0;
     const int64_t nsub = P.K >> 5;
     const int w0 = g.w0, w1 = g.w1;
     const int64_t s_begin = g.s_begin;
     const int cs = g.cs;
-    WRaw<QT> raw_own[NM][kMaxWaveSteps][kR];
-    WRaw<QT>(&raw)[NM][kMaxWaveSteps][kR] = OWN ? raw_own : raw_in;
+    WRaw<QT> raw_own[NM][WS][kR];
+    WRaw<QT>(&raw)[NM][WS][kR] = OWN ? raw_own : raw_in;
     if (OWN) issue_weights<QT, NM>(raw, P, g);
     // the epilogue's norm weight of this thread's row, fetched off the
     // critical path
@@ -660,7 +680,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
         }
         if (timed && m0 == 0 && threadIdx.x == 0) sh.t_staged = __builtin_amdgcn_s_memrealtime();
 #pragma unroll
-        for (int t = 0; t < kMaxWaveSteps; t++) {
+        for (int t = 0; t < WS; t++) {
             const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
             if (w0 + t < w1 && sb < nsub) {
                 const int sl = static_cast<int>(sb - s_begin);
@@ -687,7 +707,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
     if (timed && threadIdx.x == 0) sh.t_computed = __builtin_amdgcn_s_memrealtime();
     // The weight registers are free: the next unit's records are requested
     // now, so they stream in during this unit's reduction and epilogue.
-    if (!OWN && next >= 0) issue_weights<QT, NM, true>(raw, P, unit_geom(P, next));
+    if (!OWN && next >= 0) issue_weights<QT, NM, true>(raw, P, unit_geom<kR>(P, next));
     // The input's RMS factors (first unit of a phase) are formed now, with
     // the weight registers free: their loads are in flight during the
     // reduction below.
@@ -701,7 +721,8 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
 #pragma unroll
             for (int m = 0; m < M; m++) {
                 const float v = group8_sum(acc[mm][p][m]);
-                if (jl == 0) wpart[((wave * NM + mm) * M + m) * kRows + grp * kR + p] = v;
+                if (jl == 0)
+                    wpart[((wave * NM + mm) * M + m) * kRows + (kRows / RS) * (wave % RS) + grp * kR + p] = v;
             }
     if (rms) {
         rms_store(parts, P, M, sh.rscale);
@@ -709,15 +730,16 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit, WRaw<QT> 
         sh.rscale[threadIdx.x] = 1.0f;
     }
     lds_barrier();
-    // chunk value of (m, row) = ((w0 + w1) + w2) + w3.  A tile is final here
-    // unless K is split over units or a pair's matrices sit in two units.
+    // chunk value of (m, row): the SS step parts added in order, from waves
+    // rs, rs + RS, ... of the row's part rs.  A tile is final here unless K
+    // is split over units or a pair's matrices sit in two units.
     const bool split = P.S > 1 || (pair && NM == 1);
     for (int i = threadIdx.x; i < NM * M * kRows; i += kThreads) {
         const int mm = i / (M * kRows), r2 = i % (M * kRows), m = r2 / kRows, r = r2 % kRows;
-        float v = wpart[((0 * NM + mm) * M + m) * kRows + r];
-        v += wpart[((1 * NM + mm) * M + m) * kRows + r];
-        v += wpart[((2 * NM + mm) * M + m) * kRows + r];
-        v += wpart[((3 * NM + mm) * M + m) * kRows + r];
+        const int rs = r / (kRows / RS);
+        float v = wpart[((rs * NM + mm) * M + m) * kRows + r];
+#pragma unroll
+        for (int sp = 1; sp < SS; sp++) v += wpart[(((sp * RS + rs) * NM + mm) * M + m) * kRows + r];
         if (!split) {
             ystage[((mat + mm) * M + m) * kRows + r] = v * sh.rscale[m];
         } else {
@@ -784,8 +806,8 @@ template <int QT, int M, int NM, bool PF>
 __device__ __forceinline__ bool run_phase(const PhaseDesc &P, uint32_t u, uint32_t G, uint32_t nu, uint8_t *act,
                                           float *ystage, float *wpart, float *parts, int CS, Shared<M> &sh,
                                           unsigned *status, unsigned long long *tr) {
-    WRaw<QT> raw[NM][kMaxWaveSteps][kR];
-    if (PF) issue_weights<QT, NM, true>(raw, P, unit_geom(P, static_cast<int>(u)));
+    WRaw<QT> raw[NM][Lay::WS][Lay::R];
+    if (PF) issue_weights<QT, NM, true>(raw, P, unit_geom<Lay::R>(P, static_cast<int>(u)));
     bool first = true;
     int staged = -1;   // first step of the K chunk in LDS
     unsigned n_done = 0;
@@ -819,7 +841,8 @@ __device__ __forceinline__ bool run_phase(const PhaseDesc &P, uint32_t u, uint32
         }
         first = false;
         lds_barrier();
-        if (PF && more && next < 0) issue_weights<QT, NM, true>(raw, P, unit_geom(P, static_cast<int>(u + G)));
+        if (PF && more && next < 0)
+            issue_weights<QT, NM, true>(raw, P, unit_geom<Lay::R>(P, static_cast<int>(u + G)));
     }
     if (tr && threadIdx.x == 0) {
         tr[5] = __builtin_amdgcn_s_memrealtime();
