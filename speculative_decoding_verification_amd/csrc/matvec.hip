@@ -230,17 +230,17 @@ __device__ __forceinline__ AExt act_ext(const ARec &a) {
 template <int QT>
 __device__ __forceinline__ float block_term(const WDec &w, const ARec &a, const AExt &e, float acc) {
     if constexpr (QT == SV_Q6_K) {
-        int32_t S0 = e.o0, S1 = e.o1;
+        int32_t S0 = dot4_from(w.v[0], a.v[0], e.o0), S1 = dot4_from(w.v[4], a.v[4], e.o1);
 #pragma unroll
-        for (int k = 0; k < 4; k++) S0 = dot4(w.v[k], a.v[k], S0);
+        for (int k = 1; k < 4; k++) S0 = dot4(w.v[k], a.v[k], S0);
 #pragma unroll
-        for (int k = 4; k < 8; k++) S1 = dot4(w.v[k], a.v[k], S1);
+        for (int k = 5; k < 8; k++) S1 = dot4(w.v[k], a.v[k], S1);
         const int32_t I = __mul24(w.i0, S0) + __mul24(w.i1, S1);
         return fmaf(w.s0 * a.d, static_cast<float>(I), acc);
     } else {
-        int32_t S = 0;
+        int32_t S = dot4_first(w.v[0], a.v[0]);
 #pragma unroll
-        for (int k = 0; k < 8; k++) S = dot4(w.v[k], a.v[k], S);
+        for (int k = 1; k < 8; k++) S = dot4(w.v[k], a.v[k], S);
         if constexpr (QT == SV_Q8_0) {
             return fmaf(w.s0 * a.d, static_cast<float>(S), acc);
         } else {

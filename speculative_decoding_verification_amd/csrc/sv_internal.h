@@ -108,6 +108,20 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
 __device__ __forceinline__ int32_t dot4(uint32_t a, uint32_t b, int32_t c) {
     return __builtin_amdgcn_sdot4(static_cast<int32_t>(a), static_cast<int32_t>(b), c, false);
 }
+// First product of a dot-product chain, started at c (or at 0): the
+// three-operand encoding takes the start value as an operand, where the
+// tied two-operand form the compiler picks for the builtin first copies it
+// into the accumulator register.
+__device__ __forceinline__ int32_t dot4_from(uint32_t a, uint32_t b, int32_t c) {
+    int32_t r;
+    asm("v_dot4_i32_i8 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ int32_t dot4_first(uint32_t a, uint32_t b) {
+    int32_t r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 
 // Order-preserving map of an fp32 value to uint32 (larger float -> larger
 // key); -0 is first turned into +0 so the two compare equal.
