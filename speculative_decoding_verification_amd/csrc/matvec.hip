@@ -281,9 +281,14 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // Completion of a phase is counted in kSlots counters kSlotStride words
 // apart (unit u adds to slot u % kSlots), so finishing units do not all
-// serialise on one address; a waiter sums the slots.
+// serialise on one address; a waiter sums the slots.  The slots are kept in
+// kReplicas copies: a finishing unit adds to every copy (one instruction,
+// one lane per copy) and a waiter polls the copy of its workgroup index, so
+// each counter line serves a quarter of the polling.
 constexpr int kSlots = 8;
 constexpr int kSlotStride = 64;
+constexpr int kReplicas = 4;
+constexpr int kPhaseCounters = kSlots * kReplicas;   // counter lines per phase
 
 __device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target, unsigned *status, unsigned &abort_sh) {
     if (threadIdx.x < 64) {
@@ -295,7 +300,8 @@ __device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target,
         // sooner than with one read at a time
         // every lane reads (lanes >= kSlots repeat the first slots), so no
         // branch hides the loads from the wait-count bookkeeping
-        const unsigned *slot = ctr + (lane & (kSlots - 1)) * kSlotStride;
+        const int rep = static_cast<int>(blockIdx.x % kReplicas);
+        const unsigned *slot = ctr + (rep * kSlots + (lane & (kSlots - 1))) * kSlotStride;
         unsigned a = ld_dev(slot);
         for (;;) {
             __builtin_amdgcn_s_sleep(4);
@@ -827,8 +833,9 @@ __device__ __forceinline__ bool run_phase(const PhaseDesc &P, uint32_t u, uint32
         n_done++;
         if (counted) drain();
         lds_barrier();
+        if (counted && threadIdx.x < kReplicas)
+            add_dev(P.ready + (threadIdx.x * kSlots + u % kSlots) * kSlotStride, 1u);
         if (threadIdx.x == 0) {
-            if (counted) add_dev(P.ready + (u % kSlots) * kSlotStride, 1u);
             sh.last = 0;
             if (first && tr) {
                 tr[1] = sh.t_wait;
@@ -905,9 +912,10 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void phase_kernel(PhaseDe
     flush_best(P, sh.best, M);
 }
 
-// ctl: [1] status, [2] exited workgroups, then per phase kSlots counters of
-// finished units.  The last workgroup to exit returns every counter but the
-// status to zero, so the next run starts clean without a reset launch.
+// ctl: [1] status, [2] exited workgroups, then per phase kPhaseCounters
+// counters of finished units, kSlotStride words apart.  The last workgroup
+// to exit returns every counter but the status to zero (all its threads
+// share the stores), so the next run starts clean without a reset launch.
 template <int M>
 __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const PhaseDesc *__restrict__ table, int n_phases,
                                                         unsigned *ctl, int CS, unsigned long long *argmax,
@@ -942,13 +950,12 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const Ph
     if (cur >= 0) flush_best(P, sh.best, M);
     drain();
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = add_dev(ctl + 2, 1u);
-        if (prev == gridDim.x - 1) {
-            for (int i = kSlotStride; i < kSlotStride * (1 + n_phases * kSlots); i += kSlotStride)
-                st_dev(ctl + i, 0u);
-            st_dev(ctl + 2, 0u);
-        }
+    if (threadIdx.x == 0) sh.last = (add_dev(ctl + 2, 1u) == gridDim.x - 1) ? 1 : 0;
+    __syncthreads();
+    if (sh.last) {
+        for (int i = 1 + static_cast<int>(threadIdx.x); i < 1 + n_phases * kPhaseCounters; i += kThreads)
+            st_dev(ctl + i * kSlotStride, 0u);
+        if (threadIdx.x == 0) st_dev(ctl + 2, 0u);
     }
 }
 
@@ -1215,7 +1222,7 @@ extern "C" size_t sv_pass_workspace_bytes(const sv_phase *phases, int32_t n_phas
         max_scratch = std::max(max_scratch, sv::phase_scratch(P, M));
     }
     need += (static_cast<size_t>(n_phases) * sizeof(sv::PhaseDesc) + 255) / 256 * 256;
-    need += (static_cast<size_t>(sv::kSlotStride) * (1 + n_phases * sv::kSlots) * 4 + 255) / 256 * 256;
+    need += (static_cast<size_t>(sv::kSlotStride) * (1 + n_phases * sv::kPhaseCounters) * 4 + 255) / 256 * 256;
     need += (static_cast<size_t>(sv::kMaxGrid) * n_phases * sv::kTraceWords * 8 + 255) / 256 * 256;
     need += max_scratch;
     return need;
@@ -1237,7 +1244,7 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
     p->host.resize(n_phases);
     uint8_t *b = static_cast<uint8_t *>(workspace);
     const size_t table_bytes = (static_cast<size_t>(n_phases) * sizeof(PhaseDesc) + 255) / 256 * 256;
-    const size_t ctl_bytes = (static_cast<size_t>(kSlotStride) * (1 + n_phases * kSlots) * 4 + 255) / 256 * 256;
+    const size_t ctl_bytes = (static_cast<size_t>(kSlotStride) * (1 + n_phases * kPhaseCounters) * 4 + 255) / 256 * 256;
     p->table = reinterpret_cast<PhaseDesc *>(b);
     p->ctl = reinterpret_cast<unsigned *>(b + table_bytes);
     const size_t trace_bytes = (static_cast<size_t>(kMaxGrid) * n_phases * kTraceWords * 8 + 255) / 256 * 256;
@@ -1261,8 +1268,8 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
         }
         P.tile_count = reinterpret_cast<unsigned *>(scratch);
         P.partial = reinterpret_cast<float *>(scratch + kCounterBytes);
-        P.ready = (i + 1 < n_phases) ? p->ctl + kSlotStride * (1 + i * kSlots) : nullptr;
-        P.wait = (i > 0) ? p->ctl + kSlotStride * (1 + (i - 1) * kSlots) : nullptr;
+        P.ready = (i + 1 < n_phases) ? p->ctl + kSlotStride * (1 + i * kPhaseCounters) : nullptr;
+        P.wait = (i > 0) ? p->ctl + kSlotStride * (1 + (i - 1) * kPhaseCounters) : nullptr;
         // The next phase reads only the requantised output: with K unsplit
         // and no pairing, that comes from the units of matrix ep_src alone.
         P.count_all = (P.S > 1 || P.ep_mode != SV_EP_QUANT) ? 1 : 0;
