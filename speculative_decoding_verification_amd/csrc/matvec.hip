@@ -304,7 +304,7 @@ __device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target,
         const unsigned *slot = ctr + (rep * kSlots + (lane & (kSlots - 1))) * kSlotStride;
         unsigned a = ld_dev(slot);
         for (;;) {
-            __builtin_amdgcn_s_sleep(4);
+            __builtin_amdgcn_s_sleep(2);
             const unsigned b = ld_dev(slot);
             unsigned v = (lane < kSlots) ? a : 0u;
 #pragma unroll
