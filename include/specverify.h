@@ -163,8 +163,9 @@ typedef struct {
  * the input A (q, k, v, or gate, up).  All W[j] have the same qtype and rows,
  * and cols = A->K.  y[j] is [M][rows] fp32 or NULL.  ep may be NULL.
  * The K axis is cut into chunks whose number depends only on K; the fp32
- * combine order (sequential per lane, butterfly over a lane group, chunks
- * added in order) depends only on K, never on M, which makes every row
+ * combine order (sequential per lane, a fixed tree over a lane group, the
+ * step halves and then the chunks added in order) depends only on K, never
+ * on M, which makes every row
  * batch-invariant and every run deterministic.
  * workspace: sv_matvec_workspace_bytes(W, n_w, A) bytes, 256-byte aligned.
  * Its first 256 KiB hold tile counters that must be zero before the first
@@ -254,8 +255,10 @@ int sv_pass_status(const sv_pass *pass, uint32_t *status);
  * the input, finished its dot products, and was done (outputs written and
  * counted), when its last unit was done, the number of units it ran, when
  * the first unit had its output rows combined and when its epilogue was
- * written (0 if that unit did not run the epilogue), and three unused words
- * ([grid][n_phases][12], zero rows for phases in which a workgroup had no
+ * written (0 if that unit did not run the epilogue), the workgroup's
+ * placement (the HW_ID register in the low 32 bits, XCC_ID in the high 32),
+ * and two unused words ([grid][n_phases][12], zero rows for phases in which
+ * a workgroup had no
  * unit).  With host != NULL the last run's record is copied there
  * (synchronous; bytes >= grid * n_phases * 96).  *grid (may be NULL)
  * receives the number of workgroups a run launches. */

@@ -39,7 +39,7 @@
 namespace sv {
 
 constexpr int kThreads = 256;          // four waves
-constexpr int kRows = 32;              // rows per tile: 8 groups of 8 lanes x 4 rows
+constexpr int kRows = 32;              // rows per tile: 2 half tiles of 8 groups x 2 rows
 constexpr int kActRec = 32 + 4 + 8;     // LDS bytes per position per staged sub-block
 constexpr int kMaxChunkSteps = 12;      // most 256-element steps of K one unit covers
 constexpr int kMaxS = 8;                // most K chunks (K <= 24576)
@@ -207,7 +207,7 @@ struct ARec {
     int32_t x0, x1;  // exact sums of the codes of each 16-element half
 };
 
-// Per-position terms of a sub-block shared by the four row slots of a lane:
+// Per-position terms of a sub-block shared by the row slots of a lane:
 // Q4_K's fp32 code sum (min term), Q6_K's -32 offset of each half as the
 // starting value of that half's integer dot product.
 struct AExt {
@@ -802,7 +802,7 @@ __device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit,
 // Trace record of a (workgroup, phase): real-time counter at phase entry,
 // input ready, input staged, first unit computed, first unit done, last
 // unit done; units run; first unit reduced (partials combined), first unit's
-// epilogue written; unused.
+// epilogue written; HW_ID | XCC_ID << 32; unused.
 constexpr int kTraceWords = 12;
 
 // The units u, u + G, ... < nu of one phase on this workgroup.  A unit whose
@@ -944,7 +944,13 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const Ph
         __syncthreads();
         cur = p;
         unsigned long long *tr = trace ? trace + (static_cast<size_t>(b) * n_phases + p) * kTraceWords : nullptr;
-        if (tr && threadIdx.x == 0) tr[0] = __builtin_amdgcn_s_memrealtime();
+        if (tr && threadIdx.x == 0) {
+            tr[0] = __builtin_amdgcn_s_memrealtime();
+            // where the workgroup runs: HW_ID (CU, shader array and engine
+            // fields) and XCC_ID, full 32-bit reads of the two registers
+            tr[9] = static_cast<unsigned long long>(__builtin_amdgcn_s_getreg(0xF804)) |
+                    (static_cast<unsigned long long>(__builtin_amdgcn_s_getreg(0xF814)) << 32);
+        }
         ok = dispatch_phase<M>(P, u, G, nu, smem, ystage, wpart, parts, CS, sh, status, tr);
     }
     if (cur >= 0) flush_best(P, sh.best, M);
