@@ -161,7 +161,8 @@ typedef struct {
  * weight quants times activation quants, scaled by the block's weight and
  * activation scales (fp32), for each of n_w matrices W[0..n_w-1] that share
  * the input A (q, k, v, or gate, up).  All W[j] have the same qtype and rows,
- * and cols = A->K.  y[j] is [M][rows] fp32 or NULL.  ep may be NULL.
+ * and cols = A->K (matrices of different formats on one input are separate
+ * calls, or separate phases of a pass).  y[j] is [M][rows] fp32 or NULL.  ep may be NULL.
  * The K axis is cut into chunks whose number depends only on K; the fp32
  * combine order (sequential per lane, a fixed tree over a lane group, the
  * step halves and then the chunks added in order) depends only on K, never
@@ -206,10 +207,16 @@ int64_t sv_argmax_index(uint64_t packed);
 /* a5. A whole pass in one persistent launch.                          */
 /* ------------------------------------------------------------------ */
 /* One phase of a pass: the arguments of one sv_verify_matvec or
- * sv_head_logits call.  Phase i reads what phase i-1 wrote (its A is phase
- * i-1's epilogue output), so the phases form a chain ("Inside OpenJet
- * Engine", "One GPU launch for a speculative cycle": all phases of a cycle in
- * one launch, synchronised between phases, without host round trips). */
+ * sv_head_logits call ("Inside OpenJet Engine", "One GPU launch for a
+ * speculative cycle": all phases of a cycle in one launch, synchronised
+ * between phases, without host round trips).
+ * Dependencies follow the buffers: a phase whose A.q is the ep.q of an
+ * earlier phase waits for the latest such phase (its producer), and A.d,
+ * A.s16 and A.sumsq_parts (if given) must then be that phase's ep.d, ep.s16
+ * and ep.sumsq; a phase whose input no earlier phase writes starts at once.
+ * So phases that read one input run side by side: on a 27B-class layer,
+ * v (Q6_K, requantised for o) and q, k (Q4_K, read by nothing) are two
+ * phases on the same input, and o waits for v alone. */
 typedef struct {
     const sv_weight *W;      /* n_w matrices (read during sv_pass_create only) */
     int32_t n_w;
@@ -218,21 +225,29 @@ typedef struct {
     sv_epilogue ep;          /* ep.mode = SV_EP_NONE for none */
     const int32_t *row_ids;  /* head gather, or NULL */
     int64_t n_rows;
-    uint64_t *argmax;        /* head argmax [M], or NULL */
+    uint64_t *argmax;        /* head argmax [M], or NULL (at most 4 phases of a pass) */
 } sv_phase;
 
 typedef struct sv_pass sv_pass; /* opaque host handle */
 
-/* Device workspace for a pass: phase table, counters and partial sums. */
+/* Device workspace for a pass: phase table, control words, completion
+ * counters, trace area, and the tile counters and partial sums of every
+ * phase whose tiles are split over units (each phase has its own).  0 if a
+ * phase is invalid (sv_last_error() says why). */
 size_t sv_pass_workspace_bytes(const sv_phase *phases, int32_t n_phases);
 
-/* Validates every phase (same M for all, and K/32 divisible by 32 either for
- * all phases or for none; the epilogue outputs q, d, s16 and sumsq of all
- * phases in 256-byte blocks of their own, never shared between phases, so
- * no consumer can see a stale cached copy), writes the phase table into `workspace` (device,
- * 256-byte aligned, sv_pass_workspace_bytes bytes; it must stay allocated and
- * untouched while the pass exists) and returns a small host handle.  This
- * call synchronises with the device; it is load-time work, not per cycle. */
+/* Validates every phase (same M for all; buffers as below), writes the
+ * phase table into `workspace` (device, 256-byte aligned,
+ * sv_pass_workspace_bytes bytes; it must stay allocated and untouched while
+ * the pass exists) and returns a small host handle.  Buffer rules, checked
+ * here (SV_ERR_ARG otherwise): the requantised outputs (ep.q, d, s16, sumsq)
+ * of every phase lie in 256-byte blocks of their own, and a phase's input is
+ * either exactly an earlier phase's requantised output or shares no 256-byte
+ * block with anything the pass writes (requantised outputs, y, argmax), so
+ * no consumer can read a stale cached copy or race a writer.  When several
+ * phases write the same y buffer, the pass does not order those writes.
+ * This call synchronises with the device; it is load-time work, not per
+ * cycle. */
 int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *workspace, size_t ws_bytes,
                    sv_pass **out);
 
@@ -241,12 +256,19 @@ int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *workspace, si
  * works through the phases in order and leaves its counters reset for the
  * next run.  Allocates nothing and records no memset, so it can be captured
  * in a graph.  Runs of one pass must not overlap, and the pass expects the
- * GPU to itself while it runs (its workgroups wait on each other).  Every
- * wait between phases is bounded; if one ever expires the launch ends early
- * and sv_pass_status reports it. */
+ * GPU to itself while it runs (its workgroups wait on each other; if
+ * another kernel keeps some of them from being resident, the waits expire
+ * and the run ends early with a nonzero status instead of hanging).  Every
+ * argmax of the pass is cleared inside the launch before any head tile adds
+ * to it. */
 int sv_pass_run(const sv_pass *pass, void *stream);
 
-/* Host: status word of the last completed run (0 = ok; synchronous copy). */
+/* Host: the OR of the status of every run of this pass completed since the
+ * previous call (or since sv_pass_create); synchronises the device, then
+ * clears it.  0 = every run ok; bit 0 = a wait for a producer phase
+ * expired, bit 1 = the wait for the argmax clear expired.  A run that fails
+ * has incomplete outputs; the next run still starts clean (the live status
+ * word, counters and split tiles are reset at the end of every run). */
 int sv_pass_status(const sv_pass *pass, uint32_t *status);
 
 /* Profiling.  enable != 0 makes later runs record, per workgroup and phase,
@@ -258,10 +280,9 @@ int sv_pass_status(const sv_pass *pass, uint32_t *status);
  * written (0 if that unit did not run the epilogue), the workgroup's
  * placement (the HW_ID register in the low 32 bits, XCC_ID in the high 32),
  * and two unused words ([grid][n_phases][12], zero rows for phases in which
- * a workgroup had no
- * unit).  With host != NULL the last run's record is copied there
- * (synchronous; bytes >= grid * n_phases * 96).  *grid (may be NULL)
- * receives the number of workgroups a run launches. */
+ * a workgroup had no unit).  With host != NULL the last run's record is
+ * copied there (synchronous; bytes >= grid * n_phases * 96).  *grid (may be
+ * NULL) receives the number of workgroups a run launches. */
 int sv_pass_trace(sv_pass *pass, int enable, uint64_t *host, size_t bytes, int32_t *grid);
 
 void sv_pass_destroy(sv_pass *pass);
@@ -273,11 +294,14 @@ void sv_pass_destroy(sv_pass *pass);
  * the top token of their row; the round emits drafts[0..n-1] and then the
  * top token of row n ("How Kinetic is fast", "Why the output does not
  * change": greedy keeps a guess only when it is the model's top token).
- *   argmax [K+1] packed words from sv_head_logits; row_ids as given to it
- *   (or NULL); drafts [K] int32, 0 <= K <= 15.
- *   out [K+2] int32: out[0] = n, out[1..n+1] = emitted tokens. */
-int sv_accept_greedy(const uint64_t *argmax, const int32_t *row_ids, const int32_t *drafts,
-                     int32_t K, int32_t *out, void *stream);
+ *   argmax [K+1] packed words from sv_head_logits (or a pass); row_ids and
+ *   n_rows as given to it (row_ids NULL: n_rows = the head's rows, and the
+ *   index is the token); drafts [K] int32, 0 <= K <= 15.
+ *   out [K+2] int32: out[0] = n, out[1..n+1] = emitted tokens.  If a word
+ *   that is read was never written (0) or names an index >= n_rows, the
+ *   round is an error: out[0] = -1 and every other entry is -1. */
+int sv_accept_greedy(const uint64_t *argmax, const int32_t *row_ids, int64_t n_rows,
+                     const int32_t *drafts, int32_t K, int32_t *out, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* a8. Rejection-sampling acceptance (fp64).                           */
@@ -302,6 +326,15 @@ size_t sv_accept_workspace_bytes(int64_t V, int32_t K);
 int sv_accept_rejection(const float *logits, int64_t V, const float *q, const int32_t *drafts,
                         int32_t K, const double *u, float temperature, void *workspace,
                         size_t ws_bytes, int32_t *out, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Measurement aid (not a step of the pass).                           */
+/* ------------------------------------------------------------------ */
+/* Reads `bytes` (a multiple of 16) at src once with 16-byte streaming loads
+ * in n_sink workgroups and writes the XOR of what workgroup g read to
+ * sink[g]: the plain read rate of the device, against which the weight
+ * stream of a pass is put in context (src 16-byte aligned, device). */
+int sv_read_bandwidth(const void *src, size_t bytes, uint32_t *sink, int32_t n_sink, void *stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ EXPORTS = [
     "sv_quantize_act_q8", "sv_matvec_workspace_bytes", "sv_verify_matvec", "sv_head_workspace_bytes",
     "sv_head_logits", "sv_argmax_index", "sv_pass_workspace_bytes", "sv_pass_create", "sv_pass_run",
     "sv_pass_status", "sv_pass_trace", "sv_pass_destroy", "sv_accept_greedy", "sv_accept_workspace_bytes",
-    "sv_accept_rejection",
+    "sv_accept_rejection", "sv_read_bandwidth",
 ]
 
 
@@ -98,13 +98,14 @@ def lib():
         L.sv_pass_destroy.argtypes = [P]
         L.sv_argmax_index.restype = i64
         L.sv_argmax_index.argtypes = [ctypes.c_uint64]
-        L.sv_accept_greedy.argtypes = [P, P, P, i32, P, P]
+        L.sv_accept_greedy.argtypes = [P, P, i64, P, i32, P, P]
         L.sv_accept_workspace_bytes.restype = ctypes.c_size_t
         L.sv_accept_workspace_bytes.argtypes = [i64, i32]
         L.sv_accept_rejection.argtypes = [P, i64, P, P, i32, P, ctypes.c_float, P, ctypes.c_size_t, P, P]
+        L.sv_read_bandwidth.argtypes = [P, ctypes.c_size_t, P, i32, P]
         for f in ("sv_repack_weights", "sv_unpack_weights", "sv_quantize_act_q8", "sv_verify_matvec",
                   "sv_head_logits", "sv_accept_greedy", "sv_accept_rejection", "sv_pass_create",
-                  "sv_pass_run", "sv_pass_status"):
+                  "sv_pass_run", "sv_pass_status", "sv_read_bandwidth"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -278,9 +279,12 @@ def argmax_index(packed: int) -> int:
     return int(lib().sv_argmax_index(ctypes.c_uint64(int(packed) & 0xFFFFFFFFFFFFFFFF)))
 
 
-def accept_greedy(argmax, drafts, out, row_ids=None, stream=None):
+def accept_greedy(argmax, drafts, out, n_rows, row_ids=None, stream=None):
+    """n_rows: rows of the head the argmax words index (the vocabulary, or
+    the number of row_ids of a restricted head)."""
     K = 0 if drafts is None else drafts.numel()
-    _check(lib().sv_accept_greedy(_ptr(argmax), _ptr(row_ids), _ptr(drafts), K, _ptr(out), _stream(stream)))
+    _check(lib().sv_accept_greedy(_ptr(argmax), _ptr(row_ids), int(n_rows), _ptr(drafts), K, _ptr(out),
+                                  _stream(stream)))
 
 
 def accept_workspace_bytes(V: int, K: int) -> int:
@@ -293,3 +297,10 @@ def accept_rejection(logits, drafts, u, out, workspace, temperature=1.0, q=None,
     _check(lib().sv_accept_rejection(_ptr(logits), V, _ptr(q), _ptr(drafts), K, _ptr(u), float(temperature),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
                                      _stream(stream)))
+
+
+def read_bandwidth(src, sink, stream=None):
+    """Pure-read measurement kernel over the bytes of `src` (see
+    sv_read_bandwidth); one workgroup per element of `sink` (uint32/int32)."""
+    _check(lib().sv_read_bandwidth(_ptr(src), src.numel() * src.element_size(), _ptr(sink), sink.numel(),
+                                   _stream(stream)))

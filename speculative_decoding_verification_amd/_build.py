@@ -2,8 +2,10 @@
 
 Every HIP source is compiled for gfx950 only, with fp contraction off (the
 fused multiply-adds the kernels want are written out explicitly) and packed
-fp32 instructions disabled.  Objects go to _build/; the shared library lands
-next to this file.
+fp32 instructions disabled.  matvec_inst.hip holds the projection and pass
+kernels for one number of positions and is compiled once per M (1..16), so
+the variants build in parallel.  Objects go to _build/; the shared library
+lands next to this file.
 """
 
 from __future__ import annotations
@@ -30,13 +32,23 @@ FLAGS = [
 ]
 
 
+INST = os.path.join(CSRC, "matvec_inst.hip")
+MAX_M = 16
+
+
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    """(source, object name, extra defines) of every compile job."""
+    jobs = [(s, os.path.basename(s) + ".o", []) for s in sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+            if s != INST]
+    # the largest M first: they take longest
+    jobs = [(INST, f"matvec_inst_m{m}.o", [f"-DSV_INST_M={m}"]) for m in range(MAX_M, 0, -1)] + jobs
+    return jobs
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+def _compile(job, extra) -> str:
+    src, name, defs = job
+    obj = os.path.join(BUILD, name)
+    cmd = [HIPCC, *FLAGS, *defs, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -46,7 +58,7 @@ def _compile(src: str, extra) -> str:
 def build(verbose: bool = False, extra=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
     tmp = OUT + f".tmp{os.getpid()}"

@@ -9,6 +9,8 @@ including the next RMS normalisation's weight):
 
     x  -> a   = Q8A32(x * g1)                 (RMS factor of x folded below)
     a  -> q, k, v = r(x) W{q,k,v} a           epilogue: b = Q8A32(v * g2)
+          (when v's format differs from q and k's: one phase for v with
+          the epilogue, then one for q and k, both on a; o waits for v only)
     b  -> o   = r(v) Wo b                     epilogue: c = Q8A32(o * g3)
     c  -> g, u = r(o) W{g,u} c                epilogue: h = Q8A32((g*u) * g4)
     h  -> x'  = r(g*u) Wd h                   epilogue: Q8A32(x' * next norm)
@@ -23,6 +25,9 @@ calls are stream-ordered and allocate nothing) and replayed per cycle.
 from __future__ import annotations
 
 from dataclasses import dataclass, field
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -108,26 +113,34 @@ def upload_gguf(qtype: int, raw: np.ndarray, rows: int, cols: int, staging=None)
 class VerifyStack:
     """Device weights and buffers of one stack plus the pass itself."""
 
-    def __init__(self, shape: StackShape, weights_fn, max_M: int = 16, eps: float = 1e-6, copies: int = 1):
+    def __init__(self, shape: StackShape, weights_fn, max_M: int = 16, eps: float = 1e-6, workers: int = 0):
         """weights_fn(layer, name, qtype, rows, cols) -> GGUF bytes;
-        weights_fn(-1, 'gamma:<name>', ...) -> fp32 norm weights;
-        copies > 1 keeps several copies of every layer's weights and cycles
-        through them so consecutive passes do not hit in the caches."""
+        weights_fn(-1, 'gamma:<name>', ...) -> fp32 norm weights.  It is
+        called from `workers` threads (0: one per core, at most 16), the
+        next layer's matrices being drawn while this layer's upload."""
         t = _torch()
         self.shape, self.eps, self.max_M = shape, eps, max_M
         H, F = shape.hidden, shape.ffn
         staging = t.empty(max(repacked_bytes(qt, r, c) for _, qt, r, c in shape.layer_mats()) + 256,
                           dtype=t.uint8, device="cuda")
         self.layers = []
-        for layer in range(shape.layers):
-            lw = LayerWeights()
-            for name, qt, r, c in shape.layer_mats():
-                raw = weights_fn(layer, name, qt, r, c)
-                lw.mats[name] = upload_gguf(qt, raw, r, c, staging)
-                del raw
-            for g, n in (("g1", H), ("g2", H), ("g3", H), ("g4", F)):
-                lw.gammas[g] = t.from_numpy(weights_fn(layer, "gamma:" + g, None, n, 0)).cuda()
-            self.layers.append(lw)
+        n_workers = workers or max(1, min(16, os.cpu_count() or 1))
+        with ThreadPoolExecutor(n_workers) as ex:
+            def submit(layer):
+                return [(name, qt, r, c, ex.submit(weights_fn, layer, name, qt, r, c))
+                        for name, qt, r, c in shape.layer_mats()]
+            pending = submit(0) if shape.layers else []
+            for layer in range(shape.layers):
+                nxt = submit(layer + 1) if layer + 1 < shape.layers else []
+                lw = LayerWeights()
+                for name, qt, r, c, fut in pending:
+                    raw = fut.result()
+                    lw.mats[name] = upload_gguf(qt, raw, r, c, staging)
+                    del raw
+                for g, n in (("g1", H), ("g2", H), ("g3", H), ("g4", F)):
+                    lw.gammas[g] = t.from_numpy(weights_fn(layer, "gamma:" + g, None, n, 0)).cuda()
+                self.layers.append(lw)
+                pending = nxt
         self.gamma_f = t.from_numpy(weights_fn(-1, "gamma:final", None, H, 0)).cuda()
         self.head = None
         if shape.vocab:
@@ -166,8 +179,15 @@ class VerifyStack:
             last = li + 1 == len(L)
             nxt = self.gamma_f if last else L[li + 1].gammas["g1"]
             out = self.a_final if last else self.acts[li + 1]["in"]
-            specs.append(("qkv", [m["q"][0], m["k"][0], m["v"][0]], a["in"].desc(M, eps),
-                          [self.yq, self.yk, self.yv], a["v"].ep(SV_EP_QUANT, lw.gammas["g2"], src=2)))
+            if self.shape.attn_q == self.shape.v_q:
+                specs.append(("qkv", [m["q"][0], m["k"][0], m["v"][0]], a["in"].desc(M, eps),
+                              [self.yq, self.yk, self.yv], a["v"].ep(SV_EP_QUANT, lw.gammas["g2"], src=2)))
+            else:
+                # v (its own format) first: o waits for it alone; q and k
+                # read the same input and have no reader
+                specs.append(("v", [m["v"][0]], a["in"].desc(M, eps), [self.yv],
+                              a["v"].ep(SV_EP_QUANT, lw.gammas["g2"], src=0)))
+                specs.append(("qk", [m["q"][0], m["k"][0]], a["in"].desc(M, eps), [self.yq, self.yk], None))
             specs.append(("o", [m["o"][0]], a["v"].desc(M, eps), [None],
                           a["o"].ep(SV_EP_QUANT, lw.gammas["g3"])))
             specs.append(("gate_up", [m["gate"][0], m["up"][0]], a["o"].desc(M, eps), [None, None],
@@ -180,7 +200,7 @@ class VerifyStack:
                         gamma=self.layers[0].gammas["g1"], sumsq=self.a_in.sumsq[:M])
 
     def _accept(self, M):
-        accept_greedy(self.argmax[:M], self.drafts[:M - 1] if M > 1 else None, self.out[:M + 1])
+        accept_greedy(self.argmax[:M], self.drafts[:M - 1] if M > 1 else None, self.out[:M + 1], self.shape.vocab)
 
     def phases(self, M: int):
         """(label, callable) of every launch of one eager pass at M positions
@@ -235,6 +255,10 @@ class VerifyStack:
         H, F = sh.hidden, sh.ffn
         if label == "qkv":
             return 2 * repacked_bytes(sh.attn_q, H, H) + repacked_bytes(sh.v_q, H, H)
+        if label == "v":
+            return repacked_bytes(sh.v_q, H, H)
+        if label == "qk":
+            return 2 * repacked_bytes(sh.attn_q, H, H)
         if label == "o":
             return repacked_bytes(sh.attn_q, H, H)
         if label == "gate_up":

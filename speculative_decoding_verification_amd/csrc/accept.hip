@@ -273,13 +273,21 @@ __global__ __launch_bounds__(kCh) void acc_decide(const float *__restrict__ logi
     if (tid == 0) out[0] = n;
 }
 
+// An argmax word of 0 was never written (every packed key has a nonzero
+// part), and an index at or beyond n_rows is not a row of the head: either
+// makes the round an error (out[0] = -1, every token -1) instead of an index.
 __global__ void greedy_kernel(const unsigned long long *__restrict__ argmax, const int32_t *__restrict__ row_ids,
-                              const int32_t *__restrict__ drafts, int K, int32_t *__restrict__ out) {
+                              int64_t n_rows, const int32_t *__restrict__ drafts, int K, int32_t *__restrict__ out) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     int n = 0;
     int32_t tok = 0;
     for (int i = 0; i <= K; i++) {
-        const int64_t idx = static_cast<int64_t>(0xFFFFFFFFull - (argmax[i] & 0xFFFFFFFFull));
+        const unsigned long long w = argmax[i];
+        const int64_t idx = static_cast<int64_t>(0xFFFFFFFFull - (w & 0xFFFFFFFFull));
+        if (w == 0ull || idx >= n_rows) {
+            for (int j = 0; j < K + 2; j++) out[j] = -1;
+            return;
+        }
         tok = row_ids ? row_ids[idx] : static_cast<int32_t>(idx);
         if (i < K && drafts[i] == tok) {
             out[1 + n] = tok;
@@ -300,15 +308,16 @@ extern "C" size_t sv_accept_workspace_bytes(int64_t V, int32_t K) {
     return sv::ws_layout(V, K, &a, &b, &c);
 }
 
-extern "C" int sv_accept_greedy(const uint64_t *argmax, const int32_t *row_ids, const int32_t *drafts, int32_t K,
-                                int32_t *out, void *stream) {
+extern "C" int sv_accept_greedy(const uint64_t *argmax, const int32_t *row_ids, int64_t n_rows, const int32_t *drafts,
+                                int32_t K, int32_t *out, void *stream) {
     SV_REQUIRE(argmax && out && (K == 0 || drafts), SV_ERR_ARG, "accept_greedy: NULL buffer");
+    SV_REQUIRE(n_rows >= 1 && n_rows < (1ll << 31), SV_ERR_ARG, "accept_greedy: n_rows must be in [1, 2^31)");
     SV_REQUIRE(K >= 0 && K < SV_MAX_M, SV_ERR_ARG, "accept_greedy: K must be in [0, 15]");
     SV_REQUIRE(sv::aligned(argmax, 8) && sv::aligned(out, 4) && (!drafts || sv::aligned(drafts, 4)) &&
                    (!row_ids || sv::aligned(row_ids, 4)),
                SV_ERR_ALIGN, "accept_greedy: alignment");
     hipLaunchKernelGGL(sv::greedy_kernel, dim3(1), dim3(64), 0, sv::as_stream(stream),
-                       reinterpret_cast<const unsigned long long *>(argmax), row_ids, drafts, K, out);
+                       reinterpret_cast<const unsigned long long *>(argmax), row_ids, n_rows, drafts, K, out);
     return sv::hip_check(hipGetLastError(), "accept_greedy launch");
 }
 

@@ -1,0 +1,97 @@
+// matvec_launch.h - the phase descriptor and launch entry points shared by
+// the host side of the projection (matvec.hip) and the per-M kernel
+// instantiations (matvec_inst.hip, compiled once per M so the sixteen
+// variants build in parallel).
+#pragma once
+
+#include "sv_internal.h"
+
+namespace sv {
+
+constexpr int kThreads = 256;          // four waves
+constexpr int kRows = 32;              // rows per tile: 2 half tiles of 8 groups x 2 rows
+constexpr int kActRec = 32 + 4 + 8;    // LDS bytes per position per staged sub-block
+constexpr int kMaxChunkSteps = 12;     // most 256-element steps of K one unit covers
+constexpr int kMaxS = 8;               // most K chunks (K <= 24576)
+constexpr unsigned kSpinLimit = 1u << 22;
+constexpr int kMaxGrid = 1024;         // most workgroups a pass launches
+constexpr int kMaxArgmax = 4;          // most phases of one pass with an argmax
+constexpr int kPartsPerLane = 9;       // >= 576 RMS partials / 64 lanes
+
+// Control words of a pass (one 256-byte line, word index): the live status
+// of the running launch, the count of exited workgroups, the flag workgroup
+// 0 raises once every argmax buffer is cleared, and the status of the last
+// completed run.  The completion counters follow, from word kSlotStride on.
+constexpr int kCtlStatus = 1;
+constexpr int kCtlExited = 2;
+constexpr int kCtlArgmaxClear = 3;
+constexpr int kCtlResult = 4;
+
+// Completion of a phase is counted in kSlots counters kSlotStride words
+// apart (unit u adds to slot u % kSlots), so finishing units do not all
+// serialise on one address; a waiter sums the slots.  The slots are kept in
+// kReplicas copies: a finishing unit adds to every copy (one instruction,
+// one lane per copy) and a waiter polls the copy of its workgroup index, so
+// each counter line serves a quarter of the polling.
+constexpr int kSlots = 8;
+constexpr int kSlotStride = 64;
+constexpr int kReplicas = 4;
+constexpr int kPhaseCounters = kSlots * kReplicas;   // counter lines per phase
+
+// Trace record of a (workgroup, phase): real-time counter at phase entry,
+// input ready, input staged, first unit computed, first unit done, last
+// unit done; units run; first unit reduced (partials combined), first unit's
+// epilogue written; HW_ID | XCC_ID << 32; unused.
+constexpr int kTraceWords = 12;
+
+// Device-side description of one phase.
+struct PhaseDesc {
+    const uint8_t *w[3];
+    int32_t qtype, n_w, M;
+    int32_t N, K, wrows;
+    int32_t S, steps, n_tiles, per_tile, n_units, chunk_sub;
+    int32_t count_all;        // 0: only units of matrix ep_src feed a reader
+    int32_t fused;            // 1: a unit covers both matrices of a Q4_K gate/up pair
+    uint64_t o1, o2, o3;
+    const int32_t *row_ids;
+    const int8_t *aq;
+    const float *ad;
+    const int32_t *as16;
+    const float *in_parts;
+    int32_t n_parts;
+    float eps;
+    float *y[3];
+    int32_t ep_mode, ep_src;
+    const float *gamma;
+    int8_t *oq;
+    float *od;
+    int32_t *os16;
+    float *osumsq;
+    unsigned long long *argmax;
+    float *partial;           // [n_w][S][M][N] when the tile is split over units
+    unsigned *tile_count;     // [n_tiles], zero between calls
+    unsigned *ready;          // finished units of this phase (persistent mode; NULL: no reader)
+    const unsigned *wait;     // finished units of the input's producer (NULL: input written before)
+    uint32_t wait_target;
+    uint32_t unit_base;       // units of all earlier phases (persistent mode)
+};
+
+// The argmax buffers a pass clears before any head workgroup adds to them.
+struct ArgmaxList {
+    unsigned long long *p[kMaxArgmax];
+    int32_t M[kMaxArgmax];
+    int32_t n;
+};
+
+// Defined once per M in matvec_inst.hip.
+template <int M>
+void launch_pass_m(int grid, size_t lds, hipStream_t st, const PhaseDesc *table, int n_phases, unsigned *ctl, int CS,
+                   ArgmaxList am, unsigned long long *trace);
+template <int M>
+void launch_phase_m(int grid, size_t lds, hipStream_t st, const PhaseDesc &P, int CS);
+template <int M>
+int occupancy_pass_m(size_t lds);
+template <int M>
+hipError_t allow_lds_m(size_t lds);
+
+}  // namespace sv

@@ -135,8 +135,9 @@ def test_head_and_accept_rejects():
     assert need > 0
     _err(L.sv_head_logits(ctypes.byref(H2), ctypes.byref(A2), None, 0, FAKE, None, None, 0, None),
          sv.SV_ERR_WORKSPACE)
-    _err(L.sv_accept_greedy(FAKE, None, FAKE, 16, FAKE, None), sv.SV_ERR_ARG)
-    _err(L.sv_accept_greedy(FAKE_ODD, None, FAKE, 4, FAKE, None), sv.SV_ERR_ALIGN)
+    _err(L.sv_accept_greedy(FAKE, None, 4096, FAKE, 16, FAKE, None), sv.SV_ERR_ARG)
+    _err(L.sv_accept_greedy(FAKE, None, 0, FAKE, 4, FAKE, None), sv.SV_ERR_ARG)      # no rows
+    _err(L.sv_accept_greedy(FAKE_ODD, None, 4096, FAKE, 4, FAKE, None), sv.SV_ERR_ALIGN)
     ws = sv.accept_workspace_bytes(151936, 4)
     assert ws > 0 and ws % 256 == 0
     assert sv.accept_workspace_bytes(10, 16) == 0
@@ -167,20 +168,72 @@ def test_workspace_sizes():
             assert need == 256 * 1024 + n_w * S * M * rows * 4
 
 
+def _phase(W, A, ep=None, argmax=None):
+    ph = sv.Phase()
+    ph.W, ph.n_w, ph.A = ctypes.cast(W, ctypes.POINTER(sv.Weight)), len(W), A
+    if ep is not None:
+        ph.ep = ep
+    ph.argmax = argmax
+    return ph
+
+
 def test_pass_rejects():
     L = sv.lib()
     W1 = (sv.Weight * 1)(_w(qt=12, rows=64, cols=256))
     W2 = (sv.Weight * 1)(_w(qt=12, rows=64, cols=512))
     a1, a2 = _act(K=256), _act(M=3, K=512)
-    ph = (sv.Phase * 2)()
-    ph[0].W, ph[0].n_w, ph[0].A = ctypes.cast(W1, ctypes.POINTER(sv.Weight)), 1, a1
-    ph[1].W, ph[1].n_w, ph[1].A = ctypes.cast(W2, ctypes.POINTER(sv.Weight)), 1, a2
-    assert L.sv_pass_workspace_bytes(ph, 2) > 0
+    ph = (sv.Phase * 2)(_phase(W1, a1), _phase(W2, a2))
+    assert L.sv_pass_workspace_bytes(ph, 2) == 0          # M differs
     h = ctypes.c_void_p()
-    # M differs between phases
     _err(L.sv_pass_create(ph, 2, FAKE, 1 << 30, ctypes.byref(h)), sv.SV_ERR_SHAPE)
-    _err(L.sv_pass_create(ph, 2, FAKE, 16, ctypes.byref(h)), sv.SV_ERR_WORKSPACE)
+    ok = (sv.Phase * 1)(_phase(W1, a1))
+    need = L.sv_pass_workspace_bytes(ok, 1)
+    assert need > 0
+    _err(L.sv_pass_create(ok, 1, FAKE, need - 1, ctypes.byref(h)), sv.SV_ERR_WORKSPACE)
+    _err(L.sv_pass_create(ok, 1, FAKE_ODD, need, ctypes.byref(h)), sv.SV_ERR_ALIGN)
     _err(L.sv_pass_create(ph, 0, FAKE, 1 << 30, ctypes.byref(h)), sv.SV_ERR_ARG)
+
+
+def _buf(i):
+    """A fake, 256-byte aligned device address well apart from the others."""
+    return (1 << 32) + i * (1 << 24)
+
+
+def _ep(i, mode=sv.SV_EP_QUANT):
+    return sv.Epilogue(mode, 0, None, _buf(i), _buf(i) + (1 << 20), _buf(i) + (2 << 20), _buf(i) + (3 << 20))
+
+
+def _act_at(i, M=5, K=64, parts=False):
+    return sv.Act(M, K, _buf(i), _buf(i) + (1 << 20), _buf(i) + (2 << 20),
+                  _buf(i) + (3 << 20) if parts else None, K // 32 if parts else 0, 1e-6)
+
+
+def test_pass_dependency_rules():
+    """Rules sv_pass_create checks on the host before touching the device:
+    a consumer reads exactly its producer's outputs; inputs written by no
+    earlier phase share no 256-byte block with anything the pass writes;
+    requantised outputs never share blocks; at most four argmax phases."""
+    L = sv.lib()
+    W = (sv.Weight * 1)(_w(qt=8, rows=64, cols=64))
+    h = ctypes.c_void_p()
+
+    def create(phs):
+        arr = (sv.Phase * len(phs))(*phs)
+        return L.sv_pass_create(arr, len(phs), FAKE, 1 << 30, ctypes.byref(h))
+
+    # consumer takes the producer's codes but other scales
+    bad = _act_at(1, K=64, parts=True)
+    bad.d = _buf(7)
+    _err(create([_phase(W, _act_at(0), _ep(1)), _phase(W, bad, _ep(2))]), sv.SV_ERR_ARG)
+    # a phase's input is a later phase's output (written during the launch)
+    _err(create([_phase(W, _act_at(0), _ep(1)), _phase(W, _act_at(1), _ep(0))]), sv.SV_ERR_ARG)
+    # two phases requantise into the same buffers
+    _err(create([_phase(W, _act_at(0), _ep(1)), _phase(W, _act_at(1), _ep(1))]), sv.SV_ERR_ARG)
+    # a phase input that shares a block with an argmax the pass writes
+    _err(create([_phase(W, _act_at(0), _ep(1), argmax=_buf(0) + 128)]), sv.SV_ERR_ARG)
+    # five phases with an argmax
+    heads = [_phase(W, _act_at(0), argmax=_buf(10 + i)) for i in range(5)]
+    _err(create(heads), sv.SV_ERR_ARG)
 
 
 def test_argmax_index_decode():

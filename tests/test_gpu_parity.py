@@ -352,14 +352,14 @@ def test_accept_greedy(gu, orc, seed):
         out = gu.zeros((K + 2,), torch.int32)
         am = gu.dev(_packed(z).view(np.int64))
         dd = gu.dev(drafts) if K else None
-        sv.accept_greedy(am, dd, out)
+        sv.accept_greedy(am, dd, out, V)
         assert np.array_equal(gu.host(out), orc.accept_greedy(top, drafts))
     # restricted head: argmax positions map through the id list
     ids = np.array([5, 9, 11, 40], np.int32)
     z = np.full((3, 4), -1.0, np.float32)
     z[0, 1] = z[1, 2] = z[2, 3] = 1.0
     out = gu.zeros((4,), torch.int32)
-    sv.accept_greedy(gu.dev(_packed(z).view(np.int64)), gu.dev(np.array([9, 11], np.int32)), out,
+    sv.accept_greedy(gu.dev(_packed(z).view(np.int64)), gu.dev(np.array([9, 11], np.int32)), out, ids.size,
                      row_ids=gu.dev(ids))
     assert list(gu.host(out)) == [2, 9, 11, 40]
 
