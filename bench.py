@@ -97,14 +97,16 @@ def time_sweep(stack, Ms, steps, warmup):
         g = stack.capture(M)
         p = g._keep_pass
         p.status()                       # clears what capture's warm-up run left
+        grid = p.trace(False)
         r = time_replays(g, steps, warmup)
+        r["grid"] = grid
         st = p.status()
         if st != 0:
             raise RuntimeError(f"pass at M={M} reported status {st} during the timed replays")
         r["M"] = M
         rows.append(r)
         log(f"M={M}: {r['ms_per_pass']:.4f} ms/pass (median {r['ms_median']:.4f}, p10 {r['ms_p10']:.4f}, "
-            f"p90 {r['ms_p90']:.4f}; status ok)")
+            f"p90 {r['ms_p90']:.4f}; grid {grid}; status ok)")
         del g
     return rows
 

@@ -40,8 +40,14 @@ def sources():
     """(source, object name, extra defines) of every compile job."""
     jobs = [(s, os.path.basename(s) + ".o", []) for s in sorted(glob.glob(os.path.join(CSRC, "*.hip")))
             if s != INST]
-    # the largest M first: they take longest
-    jobs = [(INST, f"matvec_inst_m{m}.o", [f"-DSV_INST_M={m}"]) for m in range(MAX_M, 0, -1)] + jobs
+    # The kernel keeps a ring of weight records in named registers filled by
+    # one load path for every format.  LLVM's sinking of common instructions
+    # out of the per-format address branches would merge stores to different
+    # ring registers into one store through a selected pointer, which forces
+    # the ring into scratch memory; it is switched off for this file.  The
+    # largest M first: they take longest.
+    inst_flags = ["-mllvm", "-simplifycfg-sink-common=false"]
+    jobs = [(INST, f"matvec_inst_m{m}.o", [f"-DSV_INST_M={m}", *inst_flags]) for m in range(MAX_M, 0, -1)] + jobs
     return jobs
 
 

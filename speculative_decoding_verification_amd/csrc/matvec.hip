@@ -28,6 +28,7 @@ using PassFn = void (*)(int, size_t, hipStream_t, const PhaseDesc *, int, unsign
 using PhaseFn = void (*)(int, size_t, hipStream_t, const PhaseDesc &, int);
 using OccFn = int (*)(size_t);
 using LdsFn = hipError_t (*)(size_t);
+using AttrFn = hipError_t (*)(hipFuncAttributes *);
 
 template <size_t... I>
 static constexpr std::array<PassFn, SV_MAX_M> pass_fns(std::index_sequence<I...>) {
@@ -48,7 +49,33 @@ static constexpr std::array<LdsFn, SV_MAX_M> lds_fns(std::index_sequence<I...>) 
 static const std::array<PassFn, SV_MAX_M> kPassFns = pass_fns(std::make_index_sequence<SV_MAX_M>{});
 static const std::array<PhaseFn, SV_MAX_M> kPhaseFns = phase_fns(std::make_index_sequence<SV_MAX_M>{});
 static const std::array<OccFn, SV_MAX_M> kOccFns = occ_fns(std::make_index_sequence<SV_MAX_M>{});
+template <size_t... I>
+static constexpr std::array<AttrFn, SV_MAX_M> attr_fns(std::index_sequence<I...>) {
+    return {&pass_attr_m<static_cast<int>(I) + 1>...};
+}
 static const std::array<LdsFn, SV_MAX_M> kLdsFns = lds_fns(std::make_index_sequence<SV_MAX_M>{});
+static const std::array<AttrFn, SV_MAX_M> kAttrFns = attr_fns(std::make_index_sequence<SV_MAX_M>{});
+
+// Workgroups of the pass kernel one compute unit holds at once, counted
+// from what a workgroup takes: its waves against the SIMDs' wave slots and
+// its LDS against the unit's.  A SIMD holds 512 / registers-per-wave waves
+// (at most 8); the waves of a workgroup are spread over the four SIMDs, so
+// one SIMD carries ceil(waves / 4) of every workgroup (a five-wave
+// workgroup puts two on one SIMD, and two such workgroups cannot share a
+// unit whose SIMDs hold three waves each: measured).  The smaller of this
+// and the runtime's occupancy figure is used, so a grid never holds more
+// workgroups than can be resident together (they wait on each other).
+static int resident_per_cu(int M, size_t lds, const hipDeviceProp_t &prop, int occ_api) {
+    hipFuncAttributes fa;
+    if (kAttrFns[M - 1](&fa) != hipSuccess) return 0;
+    const int regs = std::max(8, (fa.numRegs + 7) / 8 * 8);
+    const int waves_simd = std::min(8, 512 / regs);
+    const int waves_wg = (kThreads + 63) / 64;
+    const int by_waves = waves_simd / ((waves_wg + 3) / 4);
+    const size_t lds_cu = prop.maxSharedMemoryPerMultiProcessor ? prop.maxSharedMemoryPerMultiProcessor : 160 * 1024;
+    const int by_lds = static_cast<int>(lds_cu / std::max<size_t>(1, lds + fa.sharedSizeBytes));
+    return std::min(std::min(occ_api, by_waves), by_lds);
+}
 
 constexpr size_t kDefaultLds = 64 * 1024;
 
@@ -82,18 +109,21 @@ static void decompose(PhaseDesc &P) {
     P.steps = static_cast<int>((nsub + 7) / 8);
     P.S = std::max(1, (P.steps + kMaxChunkSteps - 1) / kMaxChunkSteps);
     P.n_tiles = static_cast<int>((static_cast<int64_t>(P.N) + kRows - 1) / kRows);
-    // A Q4_K gate/up pair runs as one unit per (tile, chunk) for M <= 8: its
-    // records leave room in registers for both matrices.
-    P.fused = (P.ep_mode == SV_EP_PAIR && P.qtype == SV_Q4_K && P.n_w == 2 && P.M <= 8) ? 1 : 0;
+    // The matrices of a gate/up pair are units of their own; the tile's
+    // last unit forms the product.
+    P.fused = 0;
     P.per_tile = P.S * (P.fused ? 1 : P.n_w);
     P.n_units = P.n_tiles * P.per_tile;
     P.chunk_sub = ((P.steps + P.S - 1) / P.S) * 8;
 }
 
-static size_t lds_bytes(int M, int CS, int NP) {
-    const int mg = M > 8 ? 8 : M;
-    return static_cast<size_t>(mg) * CS * kActRec + static_cast<size_t>(3) * M * kRows * 4 +
-           static_cast<size_t>(8) * M * kRows * 4 + static_cast<size_t>(M) * NP * 4;
+// LDS of a workgroup: the compute waves' partial sums (two buffers), then
+// the staged input chunk of all M positions and, for an RMS-normalised
+// input, its partials; the largest phase sets the size.
+static size_t wpart_bytes(int M) { return static_cast<size_t>(2) * 8 * M * 16 * 4; }
+
+static size_t phase_lds(const PhaseDesc &P, int M) {
+    return static_cast<size_t>(M) * P.chunk_sub * kActRec + (P.in_parts ? static_cast<size_t>(M) * P.n_parts * 4 : 0);
 }
 
 static bool needs_partials(const PhaseDesc &P) { return P.S > 1 || (P.ep_mode == SV_EP_PAIR && !P.fused); }
@@ -223,7 +253,7 @@ static int launch_single(PhaseDesc &P, int M, void *ws, size_t ws_bytes, hipStre
         P.partial = reinterpret_cast<float *>(b + kCounterBytes);
     }
     const int CS = P.chunk_sub;
-    const size_t lds = lds_bytes(M, CS, P.n_parts);
+    const size_t lds = wpart_bytes(M) + phase_lds(P, M);
     int rc = prepare_lds(M, lds);
     if (rc) return rc;
     kPhaseFns[M - 1](P.n_units, lds, st, P, CS);
@@ -478,11 +508,13 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
         P.wait_target = static_cast<uint32_t>(Q.count_all ? Q.n_units : Q.n_tiles);
     }
     int chunk = 0, np = 0;
+    size_t lds = 0;
     for (auto &P : host) {
         chunk = std::max(chunk, P.chunk_sub);
         np = std::max(np, P.n_parts);
+        lds = std::max(lds, phase_lds(P, M));
     }
-    const size_t lds = lds_bytes(M, chunk, np);
+    lds += wpart_bytes(M);
     rc = prepare_lds(M, lds);
     if (rc) return rc;
     int dev = 0;
@@ -492,7 +524,7 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
     if (rc) return rc;
     // Every workgroup of the pass must be resident at once (they wait on each
     // other's phases): the grid is what the GPU holds of this kernel.
-    const int occ = kOccFns[M - 1](lds);
+    const int occ = resident_per_cu(M, lds, prop, kOccFns[M - 1](lds));
     SV_REQUIRE(occ >= 1, SV_ERR_HIP, "pass_create: the pass kernel cannot be resident with this LDS size");
     sv_pass *p = new sv_pass();
     p->M = M;

@@ -7,54 +7,142 @@
 // speculative decoding pay", section "One GPU launch for a speculative
 // cycle": weight reads serve multiple verification positions, activation
 // loads are reused across weight rows, and one launch carries the phases of
-// a cycle separated by grid-wide synchronisation).
+// a cycle separated by synchronisation between phases).
 //
 // Work decomposition.  A phase (one to three matrices sharing an input) is
-// cut into units = (32-row tile, K chunk, matrix):
-//  * K is walked in steps of 256 elements (one K-quant super-block, eight
-//    Q8_0 blocks); a chunk is at most 12 steps, so S(K) = ceil(steps / 12)
-//    depends on K alone.  Wave w takes the 16-row half tile w & 1 over the
-//    half w >> 1 of the chunk's steps, so all four waves carry the same
-//    rows x steps.
-//  * Lane j of an 8-lane row group reads sub-block 8t + j of two rows: the
-//    group reads 128 contiguous bytes of a row, and each weight record is
-//    read once and reused from registers for all M positions.  The input
-//    chunk is staged in LDS once per unit.
+// cut into units = (32-row tile, K chunk, matrix); the two matrices of a
+// gate/up pair are units of their own whose values meet in the control
+// wave of the tile's last unit.  K is walked in steps of 256 elements (one K-quant super-block,
+// eight Q8_0 blocks); a chunk is at most 20 steps (5120 elements), so
+// S(K) = ceil(steps / 20) depends on K alone.
+//
+// Roles in a workgroup.  Eight compute waves and one control wave.
+//  * Compute wave w takes the 16-row half tile w & 1 over the quarter
+//    w >> 1 of the chunk's steps.  Lane j of an 8-lane row group reads sub-block
+//    8t + j of two rows, so a group reads 128 contiguous bytes of a row, and
+//    each record is reused from registers for all M positions.  A compute
+//    wave requests its weights through a ring of items held in registers
+//    (two to four, by M): the next free item is requested as soon as
+//    an item's dot products are done, across unit and phase boundaries, so
+//    a compute wave never waits for a store or a hand-off and its loads keep
+//    streaming while the control wave synchronises.  At the end of a unit
+//    the wave writes its per-row partial sums to LDS.
+//  * The control wave never loads weights.  It waits for the phase that
+//    writes a unit's input, stages the input chunk into LDS with
+//    load-to-LDS transfers, forms the input's RMS factors, adds the compute
+//    waves' partial sums, runs the epilogue (outputs, argmax candidates,
+//    requantisation of the next input), and hands the unit off.  Its memory
+//    counter covers only its own transfers and stores, so a hand-off waits
+//    for nothing but the unit's outputs.
 // Arithmetic.  Integer block sums come from v_dot4 (exact); each block's
 // fp32 combine is a fixed sequence of operations per (row, position); a lane
 // adds its blocks in increasing order, the 8 lanes of a group are combined
-// in a fixed DPP tree, the step parts in order and the K chunks in chunk
-// order.  Nothing depends on M or on which workgroup ran which unit,
+// in a fixed DPP tree, the four step quarters in order and the K chunks in
+// chunk order.  Nothing depends on M or on which workgroup ran which unit,
 // so every output row is bit-identical to the same row computed alone, and
 // runs are deterministic.
-// Scheduling.  Single calls launch one workgroup per unit.  A whole pass
-// runs as one persistent launch sized to the number of workgroups the GPU
-// holds at once: the units of each phase are dealt round-robin, and a
-// workgroup issues a unit's weight loads before it waits until the phase its
-// input comes from has handed off.  All waits are bounded.
+// Scheduling.  A pass runs as one persistent launch sized to the number of
+// workgroups the GPU holds at once; the units of each phase are dealt
+// round-robin, continuing where the previous phase stopped.  A single call
+// launches one workgroup per unit.  Every wait is bounded.
 #pragma once
-#include <algorithm>
-#include <vector>
 
 #include "matvec_launch.h"
 
 namespace sv {
 
+#define SV_AS3 __attribute__((address_space(3)))
+#define SV_AS4 __attribute__((address_space(4)))
 
-// Lane layout of a unit: R rows per lane; the tile's rows are cut into
-// RS = 4 / R parts and the chunk's steps into SS = 4 / RS parts, wave w
-// taking row part w % RS over step part w / RS (at most WS steps).  Two rows
-// per lane give every wave the same rows x steps (a chunk's step count is
-// rarely a multiple of four).  The layout fixes the order of the fp32 sums,
-// so it must not depend on M: each position's result is bitwise the same at
-// every M.
-struct Lay {
-    static constexpr int R = 2;
-    static constexpr int RS = 4 / R;
-    static constexpr int SS = 4 / RS;
-    static constexpr int WS = kMaxChunkSteps / SS;
+constexpr int kCompWaves = 8;
+constexpr int kStepParts = kCompWaves / 2;   // compute waves per half tile
+
+// Ring depth (items in flight per compute wave) by M: deeper rings for few
+// positions, where a wave's dot products leave registers free.  It changes
+// no result.
+template <int M>
+struct RingDepth {
+    static constexpr int value = M <= 2 ? 4 : (M <= 5 ? 3 : 2);
 };
 
+// ------------------------------------------------------------ tables
+// Phase descriptors are read with scalar loads: from the pass's table in
+// device memory through a constant-address-space pointer, or from the
+// kernel argument of a single call.
+struct ManyTab {
+    const SV_AS4 PhaseDesc *t;
+    __device__ __forceinline__ const SV_AS4 PhaseDesc &operator[](int p) const { return t[p]; }
+};
+struct OneTab {
+    PhaseDesc P;
+    __device__ __forceinline__ const PhaseDesc &operator[](int) const { return P; }
+};
+
+// The units of phase p that workgroup b of G runs: u0, u0 + G, ... < n_units.
+struct UnitCur {
+    int p;
+    uint32_t u;
+};
+
+template <class Tab>
+__device__ __forceinline__ void unit_seek(const Tab &tab, int n_phases, uint32_t b, uint32_t G, UnitCur &c) {
+    for (; c.p < n_phases; c.p++) {
+        const uint32_t base = static_cast<uint32_t>(tab[c.p].unit_base);
+        c.u = (b + G - base % G) % G;
+        if (c.u < static_cast<uint32_t>(tab[c.p].n_units)) return;
+    }
+}
+template <class Tab>
+__device__ __forceinline__ void unit_first(const Tab &tab, int n_phases, uint32_t b, uint32_t G, UnitCur &c) {
+    c.p = 0;
+    c.u = 0;
+    unit_seek(tab, n_phases, b, G, c);
+}
+template <class Tab>
+__device__ __forceinline__ void unit_next(const Tab &tab, int n_phases, uint32_t b, uint32_t G, UnitCur &c) {
+    c.u += G;
+    if (c.u < static_cast<uint32_t>(tab[c.p].n_units)) return;
+    c.p++;
+    unit_seek(tab, n_phases, b, G, c);
+}
+
+// Geometry of a unit: tile, K chunk and matrix; the chunk's steps [c0, c1)
+// and its staged sub-blocks [s_begin, s_begin + cs).
+struct UnitPos {
+    int tile, chunk, mat, c0, c1, s_begin, cs;
+};
+template <class PD>
+__device__ __forceinline__ UnitPos unit_pos(const PD &P, uint32_t u) {
+    UnitPos g;
+    const int per_tile = P.per_tile, S = P.S, steps = P.steps;
+    g.tile = static_cast<int>(u) / per_tile;
+    const int rem = static_cast<int>(u) % per_tile;
+    g.chunk = rem % S;
+    g.mat = rem / S;
+    g.c0 = g.chunk * steps / S;
+    g.c1 = (g.chunk + 1) * steps / S;
+    const int nsub = P.K >> 5;
+    g.s_begin = g.c0 * 8;
+    g.cs = min((g.c1 - g.c0) * 8, nsub - g.s_begin);
+    return g;
+}
+
+// Steps [w0, w1) of compute wave `wave`, and the number of ring items they
+// make (at least one: a wave with no step still passes through the unit).
+// A Q4_K record of one matrix is 5 words, so its items carry two steps.
+struct WaveSpan {
+    int w0, w1, sp, nitems;
+};
+template <class PD>
+__device__ __forceinline__ WaveSpan wave_span(const PD &P, const UnitPos &g, int wave) {
+    WaveSpan s;
+    const int tc = g.c1 - g.c0, part = wave >> 1;
+    s.w0 = g.c0 + part * tc / kStepParts;
+    s.w1 = g.c0 + (part + 1) * tc / kStepParts;
+    s.sp = P.qtype == SV_Q4_K ? 2 : 1;
+    s.nitems = max(1, (s.w1 - s.w0 + s.sp - 1) / s.sp);
+    return s;
+}
 
 // ------------------------------------------------------------ weights
 template <int QT>
@@ -79,23 +167,61 @@ struct WRaw<SV_Q6_K> {
     uint32_t sc, d;
 };
 
-template <int QT>
-__device__ __forceinline__ void load_w(WRaw<QT> &r, const uint8_t *__restrict__ w, const PhaseDesc &P, int64_t row,
-                                       int64_t s) {
-    const int64_t K = P.K, nsub = K >> 5;
+// One item of the ring: the raw records of a lane in named registers (every
+// index below is a template parameter, so nothing is ever addressed by a
+// runtime index, which would put the ring in memory).  An item is always the
+// same twelve loads into the same registers, four of 16 bytes (quads q0-q3)
+// and eight of 2 bytes (half-words h0-h7); only their addresses depend on
+// the format.  So the loads in flight never depend on the path taken, and
+// the compiler's wait before a slot is read covers that slot alone.
+//   Q4_K (record i = 2 step + row, or for a pair 2 matrix + row): quants in
+//        quad i, the lane's header dword in h(2i) | h(2i + 1) << 16
+//   Q6_K (row p < 2): low nibbles in quad p, high bits in the first 8 bytes
+//        of quad 2 + p, the two int8 sub-scales in h(p), d in h(2 + p)
+//   Q8_0 (row p < 2): quants in quads 2p and 2p + 1, d in h(p)
+// Half-words a format does not use repeat an earlier address.
+struct Slot {
+    uint4 q0, q1, q2, q3;
+    uint32_t h0, h1, h2, h3, h4, h5, h6, h7;
+};
+
+template <int I>
+__device__ __forceinline__ const uint4 &quad(const Slot &s) {
+    if constexpr (I == 0) return s.q0;
+    else if constexpr (I == 1) return s.q1;
+    else if constexpr (I == 2) return s.q2;
+    else return s.q3;
+}
+template <int I>
+__device__ __forceinline__ uint32_t half(const Slot &s) {
+    if constexpr (I == 0) return s.h0;
+    else if constexpr (I == 1) return s.h1;
+    else if constexpr (I == 2) return s.h2;
+    else if constexpr (I == 3) return s.h3;
+    else if constexpr (I == 4) return s.h4;
+    else if constexpr (I == 5) return s.h5;
+    else if constexpr (I == 6) return s.h6;
+    else return s.h7;
+}
+
+template <int QT, int I>
+__device__ __forceinline__ WRaw<QT> rec_of(const Slot &s) {
+    WRaw<QT> r;
     if constexpr (QT == SV_Q8_0) {
-        r.q0 = gld16_nt(w + row * K + s * 32);
-        r.q1 = gld16_nt(w + row * K + s * 32 + 16);
-        r.d = gld(reinterpret_cast<const uint16_t *>(w + P.o1 + (row * nsub + s) * 2));
+        r.q0 = quad<2 * I>(s);
+        r.q1 = quad<2 * I + 1>(s);
+        r.d = half<I>(s);
     } else if constexpr (QT == SV_Q4_K) {
-        r.q = gld16_nt(w + (row * nsub + s) * 16);
-        r.h = gld(reinterpret_cast<const uint32_t *>(w + P.o1 + (row * (K >> 8) + (s >> 3)) * 16) + (s & 3));
+        r.q = quad<I>(s);
+        r.h = half<2 * I>(s) | (half<2 * I + 1>(s) << 16);
     } else {
-        r.l = gld16_nt(w + (row * nsub + s) * 16);
-        r.h = gld8_nt(w + P.o1 + (row * nsub + s) * 8);
-        r.sc = gld(reinterpret_cast<const uint16_t *>(w + P.o2 + row * (K >> 4) + 2 * s));
-        r.d = gld(reinterpret_cast<const uint16_t *>(w + P.o3 + (row * (K >> 8) + (s >> 3)) * 2));
+        r.l = quad<I>(s);
+        const uint4 hq = quad<2 + I>(s);
+        r.h = make_uint2(hq.x, hq.y);
+        r.sc = half<I>(s);
+        r.d = half<2 + I>(s);
     }
+    return r;
 }
 
 // Unpacked weights of one row slot for one sub-block: eight dwords of int8
@@ -178,7 +304,6 @@ struct AExt {
     float xf;
     int32_t o0, o1;
 };
-template <int QT>
 __device__ __forceinline__ AExt act_ext(const ARec &a) {
     AExt e;
     e.xf = static_cast<float>(a.x0 + a.x1);
@@ -214,139 +339,36 @@ __device__ __forceinline__ float block_term(const WDec &w, const ARec &a, const 
     }
 }
 
-// LDS record of the staged activation chunk, per position: [CS] 16-byte low
-// halves, [CS] 16-byte high halves, [CS] fp32 scales, [CS] 8-byte sums.
-__device__ __forceinline__ void read_act(ARec &r, const uint8_t *act_m, int CS, int sl) {
-    const uint4 lo = *reinterpret_cast<const uint4 *>(act_m + sl * 16);
-    const uint4 hi = *reinterpret_cast<const uint4 *>(act_m + CS * 16 + sl * 16);
+// LDS layout of a staged chunk of cs sub-blocks of all M positions: codes
+// [M][cs][32] (the global bytes as they are), scales [M][cs] fp32, code sums
+// [M][cs][2] int32; the RMS partials of the input follow, [M][n_parts].
+struct ActLds {
+    const uint8_t *q;
+    const float *d;
+    const int2 *x;
+    int cs;
+};
+__device__ __forceinline__ ActLds act_lds(const uint8_t *act, int M, int cs) {
+    ActLds a;
+    a.q = act;
+    a.d = reinterpret_cast<const float *>(act + M * cs * 32);
+    a.x = reinterpret_cast<const int2 *>(act + M * cs * 36);
+    a.cs = cs;
+    return a;
+}
+__device__ __forceinline__ void read_act(ARec &r, const ActLds &A, int m, int sl) {
+    const uint8_t *q = A.q + (m * A.cs + sl) * 32;
+    const uint4 lo = *reinterpret_cast<const uint4 *>(q);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(q + 16);
     r.v[0] = lo.x; r.v[1] = lo.y; r.v[2] = lo.z; r.v[3] = lo.w;
     r.v[4] = hi.x; r.v[5] = hi.y; r.v[6] = hi.z; r.v[7] = hi.w;
-    r.d = reinterpret_cast<const float *>(act_m + CS * 32)[sl];
-    const int2 x = reinterpret_cast<const int2 *>(act_m + CS * 36)[sl];
+    r.d = A.d[m * A.cs + sl];
+    const int2 x = A.x[m * A.cs + sl];
     r.x0 = x.x;
     r.x1 = x.y;
 }
 
-// Shared state of a workgroup.
-template <int M>
-struct Shared {
-    float rscale[SV_MAX_M];
-    unsigned long long best[SV_MAX_M];
-    int last;
-    unsigned abort;
-    unsigned long long t_wait, t_staged, t_computed, t_reduced, t_epi;   // first unit of a phase (trace)
-};
-
-// Workgroup barrier for LDS data only: waits for this wave's LDS
-// operations, not for its outstanding global loads (a full __syncthreads
-// would also wait for weight records already requested for the next unit).
-// No global memory written before it is read by another wave after it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-
-__device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target, unsigned *status, unsigned &abort_sh) {
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        unsigned n = 0;
-        bool ok = true;
-        // two polls in flight: the next read is issued before the previous
-        // one is examined, so an update is seen about half a round trip
-        // sooner than with one read at a time
-        // every lane reads (lanes >= kSlots repeat the first slots), so no
-        // branch hides the loads from the wait-count bookkeeping
-        const int rep = static_cast<int>(blockIdx.x % kReplicas);
-        const unsigned *slot = ctr + (rep * kSlots + (lane & (kSlots - 1))) * kSlotStride;
-        unsigned a = ld_dev(slot);
-        for (;;) {
-            __builtin_amdgcn_s_sleep(2);
-            const unsigned b = ld_dev(slot);
-            unsigned v = (lane < kSlots) ? a : 0u;
-#pragma unroll
-            for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-            v = __shfl(v, 0, 64);
-            if (v >= target) break;
-            if (++n > kSpinLimit || ((n & 63u) == 0u && ld_dev(status) != 0u)) {
-                ok = false;
-                break;
-            }
-            a = b;
-        }
-        if (lane == 0) {
-            if (!ok) or_dev(status, 1u);
-            abort_sh = ok ? 0u : 1u;
-        }
-    }
-    __syncthreads();
-    return abort_sh == 0u;
-}
-
-
-// Stage positions [m0, m0 + mg) of the chunk's sub-blocks [s0, s0 + cs) into
-// LDS.  Thread t takes items t, t + 256, ... of the 16-byte halves and of the
-// (scale, sums) records; every global load of a thread is issued before the
-// first one is stored.  The item index i splits into (position, offset) as
-// i / D = (i * ceil(2^20 / D)) >> 20, exact for i < 2^11 and D <= 512 (the
-// rounding error i / 2^20 stays below 1 / D), so no lane divides.
-constexpr int kStageHalf = 6;   // >= 8 positions * 96 sub-blocks * 2 halves / 256 threads
-constexpr int kStageRec = 3;    // >= 8 * 96 / 256
-
-__device__ __forceinline__ void stage_act(uint8_t *act, const PhaseDesc &P, int m0, int mg, int64_t s0, int cs,
-                                          int CS) {
-    const int64_t K = P.K, nsub = K >> 5;
-    const int nhalf = mg * cs * 2, nrec = mg * cs;
-    const uint32_t D2 = 2u * static_cast<uint32_t>(cs), D1 = static_cast<uint32_t>(cs);
-    const uint32_t mul2 = ((1u << 20) + D2 - 1) / D2, mul1 = ((1u << 20) + D1 - 1) / D1;
-    // named registers, not arrays: a private array here ends up in scratch
-    uint4 h0, h1, h2, h3, h4, h5;
-#define SV_HALF(k)                                                                                       \
-    const int i = threadIdx.x + (k) * kThreads;                                                          \
-    const int m = static_cast<int>(__umul24(static_cast<uint32_t>(i), mul2) >> 20);                      \
-    const int r = i - m * static_cast<int>(D2), sl = r >> 1, h = r & 1;
-#define SV_LDH(k, hv)                                                                                    \
-    {                                                                                                    \
-        SV_HALF(k)                                                                                       \
-        if (i < nhalf) hv = gld16(P.aq + (m0 + m) * K + (s0 + sl) * 32 + h * 16);                         \
-    }
-    SV_LDH(0, h0) SV_LDH(1, h1) SV_LDH(2, h2) SV_LDH(3, h3) SV_LDH(4, h4) SV_LDH(5, h5)
-#undef SV_LDH
-    float d0, d1, d2;
-    uint2 x0, x1, x2;
-#define SV_REC(k)                                                                                        \
-    const int i = threadIdx.x + (k) * kThreads;                                                          \
-    const int m = static_cast<int>(__umul24(static_cast<uint32_t>(i), mul1) >> 20);                      \
-    const int sl = i - m * static_cast<int>(D1);
-#define SV_LDR(k, dv, xv)                                                                                \
-    {                                                                                                    \
-        SV_REC(k)                                                                                        \
-        if (i < nrec) {                                                                                  \
-            dv = gld(P.ad + (m0 + m) * nsub + s0 + sl);                                                  \
-            xv = gld8(P.as16 + (m0 + m) * (K >> 4) + 2 * (s0 + sl));                                     \
-        }                                                                                                \
-    }
-    SV_LDR(0, d0, x0) SV_LDR(1, d1, x1) SV_LDR(2, d2, x2)
-#undef SV_LDR
-#define SV_STH(k, hv)                                                                                    \
-    {                                                                                                    \
-        SV_HALF(k)                                                                                       \
-        if (i < nhalf) *reinterpret_cast<uint4 *>(act + m * CS * kActRec + h * CS * 16 + sl * 16) = hv;    \
-    }
-    SV_STH(0, h0) SV_STH(1, h1) SV_STH(2, h2) SV_STH(3, h3) SV_STH(4, h4) SV_STH(5, h5)
-#undef SV_STH
-#define SV_STR(k, dv, xv)                                                                                \
-    {                                                                                                    \
-        SV_REC(k)                                                                                        \
-        if (i < nrec) {                                                                                  \
-            uint8_t *am = act + m * CS * kActRec;                                                        \
-            reinterpret_cast<float *>(am + CS * 32)[sl] = dv;                                            \
-            reinterpret_cast<uint2 *>(am + CS * 36)[sl] = xv;                                            \
-        }                                                                                                \
-    }
-    SV_STR(0, d0, x0) SV_STR(1, d1, x1) SV_STR(2, d2, x2)
-#undef SV_STR
-#undef SV_HALF
-#undef SV_REC
-}
-
+// ------------------------------------------------------------ lane sums
 // Sums over lanes with data-parallel primitives (no LDS traffic), in a fixed
 // order.  DPP controls: quad_perm, row_shl:n = 0x100 + n, row_ror:n = 0x120 + n.
 template <int CTRL>
@@ -374,35 +396,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
     return ((r0 + r1) + r2) + r3;
 }
-
-// RMS factors r = 1 / sqrt(sum / K + eps) of the input rows from its
-// per-block sums of squares.  rms_fetch copies the M x n_parts partials into
-// LDS with the loads' LDS transfer (no registers held), issued with the
-// input staging; after the barrier that ends staging, rms_store has wave w
-// take positions w + 4 k: lane l adds partials l, l + 64, ... in order, then
-// wave_sum.  A fixed order that depends only on the number of partials.
-__device__ __forceinline__ void rms_fetch(float *parts, const PhaseDesc &P, int M) {
-    const int lane = threadIdx.x & 63;
-    const int wave = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
-    const int total = M * P.n_parts;
-    for (int k = wave; 64 * k < total; k += 4) {
-        const int f = 64 * k + lane;
-        if (f < total)
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(P.in_parts + f),
-                                             (__attribute__((address_space(3))) void *)(parts + 64 * k), 4, 0, 0);
-    }
-}
-
-__device__ __forceinline__ void rms_store(const float *parts, const PhaseDesc &P, int M, float *rs) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int m = wave; m < M; m += 4) {
-        float t = 0.0f;
-        for (int i = lane; i < P.n_parts; i += 64) t += parts[m * P.n_parts + i];
-        const float tot = wave_sum(t);
-        if (lane == 0) rs[m] = 1.0f / sqrtf(tot / static_cast<float>(P.K) + P.eps);
-    }
-}
-
 // Reductions over the 32 lanes of a half-wave (every lane gets the result):
 // within each row of 16 by DPP, then the two rows by one lane exchange.
 __device__ __forceinline__ float half_max(float v) {
@@ -445,454 +438,770 @@ __device__ __forceinline__ unsigned long long half_max64(unsigned long long v) {
     return umax64(v, __shfl_xor(v, 16, 64));
 }
 
-// Epilogue of a finished row tile (LDS ystage [n_w][M][kRows]): y outputs
-// of the matrices in [mat_lo, mat_hi), argmax candidates and the requantised
-// next activation.  Half-wave h takes positions h, h + 8 (lane = row).
+// Workgroup barrier for LDS data only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a full __syncthreads
+// would also wait for the weight records already requested).  No global
+// memory written before it is read by another wave after it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ------------------------------------------------------------ shared state
 template <int M>
-__device__ __forceinline__ void finish_tile(const PhaseDesc &P, const float *ystage, int64_t row0, int mat_lo,
-                                            int mat_hi, bool do_ep, float g_row, Shared<M> &sh) {
-    const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), static_cast<int64_t>(P.N) - row0));
-    for (int mat = mat_lo; mat < mat_hi; mat++) {
-        float *y = P.y[mat];
-        if (!y) continue;
-        for (int i = threadIdx.x; i < M * kRows; i += kThreads) {
-            const int m = i / kRows, r = i % kRows;
-            if (r < rows_here) gst(y + static_cast<int64_t>(m) * P.N + row0 + r, ystage[(mat * M + m) * kRows + r]);
+struct Shared {
+    float rscale[SV_MAX_M];
+    unsigned long long best[SV_MAX_M];
+    unsigned abort;
+};
+
+// Dynamic LDS: wave partials [2 buffers][8 waves][M][16 rows] fp32, then
+// the staged input chunk and its RMS partials.
+template <int M>
+__device__ __forceinline__ float *wpart_buf(uint8_t *smem, int buf) {
+    return reinterpret_cast<float *>(smem) + buf * (kCompWaves * M * 16);
+}
+template <int M>
+__device__ __forceinline__ uint8_t *act_base(uint8_t *smem) {
+    return smem + 2 * kCompWaves * M * 16 * 4;
+}
+
+// Trace record of a (workgroup, phase) (control wave): real-time counter at
+// the first unit of the phase, input ready, input staged, first unit
+// computed, first unit handed off, last unit handed off; units run; unused
+// x2; HW_ID | XCC_ID << 32; unused x2.
+__device__ __forceinline__ unsigned long long now() { return __builtin_amdgcn_s_memrealtime(); }
+
+// ============================================================ compute waves
+// The item cursor of a compute wave: unit, its geometry, the item inside
+// it, and the phase fields the loads and the dot products need.
+struct ItemCur {
+    UnitCur uc;
+    int item;
+    // phase
+    const uint8_t *w0, *w1, *w2;
+    const uint8_t *wm;   // matrix of the current unit
+    int qtype, K, N, wrows;
+    uint64_t o1, o2, o3;
+    const int32_t *row_ids;
+    // unit
+    UnitPos g;
+    WaveSpan s;
+    bool sync;        // a barrier opens this unit (new phase or new chunk)
+    int64_t srow[2];  // rows this lane reads (load cursor only)
+};
+
+template <class Tab>
+__device__ __forceinline__ void cur_phase(const Tab &tab, ItemCur &c) {
+    const auto &P = tab[c.uc.p];
+    c.w0 = P.w[0];
+    c.w1 = P.w[1];
+    c.w2 = P.w[2];
+    c.qtype = P.qtype;
+    c.K = P.K;
+    c.N = P.N;
+    c.wrows = P.wrows;
+    c.o1 = P.o1;
+    c.o2 = P.o2;
+    c.o3 = P.o3;
+    c.row_ids = P.row_ids;
+}
+
+// Rows of this lane in the unit: 2 grp + p of the wave's half tile, mapped
+// through row_ids (read with scalar loads, so they never wait on the ring's
+// weight records) and clamped into the matrix.
+__device__ __forceinline__ void cur_rows(ItemCur &c, int wave) {
+    const int lane = threadIdx.x & 63, grp = lane >> 3;
+    const int64_t rw = static_cast<int64_t>(c.g.tile) * kRows + 16 * (wave & 1);
+    if (c.row_ids) {
+        const SV_AS4 int32_t *ids = reinterpret_cast<const SV_AS4 int32_t *>(reinterpret_cast<uintptr_t>(c.row_ids));
+        int32_t id[16];
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+            const int64_t r = rw + k;
+            id[k] = ids[r < c.N ? r : 0];
+        }
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            int32_t v = id[p];
+#pragma unroll
+            for (int k = 1; k < 8; k++)
+                if (grp == k) v = id[2 * k + p];
+            c.srow[p] = (v < 0 || v >= c.wrows) ? 0 : v;
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+            const int64_t r = rw + grp * 2 + p;
+            c.srow[p] = r < c.N ? r : 0;
         }
     }
-    const int hw = threadIdx.x >> 5, l32 = threadIdx.x & 31;
-    if (P.argmax) {
-        for (int m = hw; m < M; m += kThreads / 32) {
+}
+
+template <class Tab>
+__device__ __forceinline__ void cur_unit(const Tab &tab, ItemCur &c, int wave, bool phase_changed, int prev_chunk,
+                                         bool rows) {
+    const auto &P = tab[c.uc.p];
+    c.g = unit_pos(P, c.uc.u);
+    c.s = wave_span(P, c.g, wave);
+    c.item = 0;
+    c.sync = phase_changed || c.g.chunk != prev_chunk;
+    // integer arithmetic, not a select: a select among the three fields is
+    // turned into an indexed load, which puts the whole cursor in memory
+    const uint64_t m0 = c.g.mat == 0, m1 = c.g.mat == 1, m2 = c.g.mat == 2;
+    c.wm = reinterpret_cast<const uint8_t *>(m0 * reinterpret_cast<uint64_t>(c.w0) +
+                                             m1 * reinterpret_cast<uint64_t>(c.w1) +
+                                             m2 * reinterpret_cast<uint64_t>(c.w2));
+    if (rows) cur_rows(c, wave);
+}
+
+template <class Tab>
+__device__ __forceinline__ bool cur_init(const Tab &tab, int n_phases, uint32_t b, uint32_t G, ItemCur &c, int wave,
+                                         bool rows) {
+    unit_first(tab, n_phases, b, G, c.uc);
+    if (c.uc.p >= n_phases) return false;
+    cur_phase(tab, c);
+    cur_unit(tab, c, wave, true, -1, rows);
+    return true;
+}
+
+// Next item; false at the end of the workgroup's units.
+template <class Tab>
+__device__ __forceinline__ bool cur_advance(const Tab &tab, int n_phases, uint32_t b, uint32_t G, ItemCur &c,
+                                            int wave, bool rows) {
+    if (++c.item < c.s.nitems) return true;
+    const int p0 = c.uc.p, chunk0 = c.g.chunk;
+    unit_next(tab, n_phases, b, G, c.uc);
+    if (c.uc.p >= n_phases) return false;
+    if (c.uc.p != p0) cur_phase(tab, c);
+    cur_unit(tab, c, wave, c.uc.p != p0, chunk0, rows);
+    return true;
+}
+
+// Like cur_advance, but at the end of the sequence the cursor stays on the
+// last item (the load cursor then re-reads it; see ring_step).
+template <class Tab>
+__device__ __forceinline__ bool cur_advance_keep(const Tab &tab, int n_phases, uint32_t b, uint32_t G, ItemCur &c,
+                                                 int wave, bool rows) {
+    if (c.item + 1 < c.s.nitems) {
+        c.item++;
+        return true;
+    }
+    UnitCur nx = c.uc;
+    unit_next(tab, n_phases, b, G, nx);
+    if (nx.p >= n_phases) return false;
+    const int p0 = c.uc.p, chunk0 = c.g.chunk;
+    c.uc = nx;
+    if (c.uc.p != p0) cur_phase(tab, c);
+    cur_unit(tab, c, wave, c.uc.p != p0, chunk0, rows);
+    return true;
+}
+
+// Requests the records of the cursor's item into slot s.  Every item
+// issues the same loads whether or not its steps exist (a missing step reads
+// the chunk's first sub-block again and is never used), so the number of
+// loads in flight does not depend on the data.
+__device__ __forceinline__ int64_t item_sb(const ItemCur &c, int t, int64_t fallback) {
+    const int64_t nsub = c.K >> 5;
+    const int64_t sb = static_cast<int64_t>(t) * 8 + (threadIdx.x & 7);
+    return (t < c.s.w1 && sb < nsub) ? sb : fallback;
+}
+
+__device__ __forceinline__ uint4 q16(const uint8_t *p) { return gld16_nt(p); }
+__device__ __forceinline__ uint32_t h2(const uint8_t *p) { return gld(reinterpret_cast<const uint16_t *>(p)); }
+
+__device__ __forceinline__ void load_item(Slot &s, const ItemCur &c) {
+    const int jl = threadIdx.x & 7;
+    const int64_t r0 = c.srow[0], r1 = c.srow[1];
+    const int64_t K = c.K, nsub = K >> 5, nsb = K >> 8;
+    const bool q4 = c.qtype == SV_Q4_K;
+    const int t = c.s.w0 + c.item * (q4 ? 2 : 1);
+    const int64_t fb = c.g.s_begin + (c.qtype == SV_Q8_0 ? 0 : jl);
+    const int64_t sa = item_sb(c, t, fb);
+    const int64_t sb = q4 ? item_sb(c, t + 1, fb) : sa;
+    const uint8_t *a0, *a1, *a2, *a3, *b0, *b1, *b2, *b3, *b4, *b5, *b6, *b7;
+    if (q4) {
+        // records: (r0, sa), (r1, sa), (r0, sb), (r1, sb)
+        const uint8_t *w = c.wm;
+        a0 = w + (r0 * nsub + sa) * 16;
+        a1 = w + (r1 * nsub + sa) * 16;
+        a2 = w + (r0 * nsub + sb) * 16;
+        a3 = w + (r1 * nsub + sb) * 16;
+        const int64_t lh = (sa & 3) * 4, lh2 = (sb & 3) * 4;
+        b0 = w + c.o1 + (r0 * nsb + (sa >> 3)) * 16 + lh;
+        b2 = w + c.o1 + (r1 * nsb + (sa >> 3)) * 16 + lh;
+        b4 = w + c.o1 + (r0 * nsb + (sb >> 3)) * 16 + lh2;
+        b6 = w + c.o1 + (r1 * nsb + (sb >> 3)) * 16 + lh2;
+        b1 = b0 + 2;
+        b3 = b2 + 2;
+        b5 = b4 + 2;
+        b7 = b6 + 2;
+    } else if (c.qtype == SV_Q6_K) {
+        a0 = c.wm + (r0 * nsub + sa) * 16;
+        a1 = c.wm + (r1 * nsub + sa) * 16;
+        // 16 bytes from the 8-byte high-bit record: the stream is followed by
+        // the scale streams, so the extra 8 bytes stay inside the matrix
+        a2 = c.wm + c.o1 + (r0 * nsub + sa) * 8;
+        a3 = c.wm + c.o1 + (r1 * nsub + sa) * 8;
+        b0 = c.wm + c.o2 + r0 * (K >> 4) + 2 * sa;
+        b1 = c.wm + c.o2 + r1 * (K >> 4) + 2 * sa;
+        b2 = c.wm + c.o3 + (r0 * nsb + (sa >> 3)) * 2;
+        b3 = c.wm + c.o3 + (r1 * nsb + (sa >> 3)) * 2;
+        b4 = b0;
+        b5 = b1;
+        b6 = b2;
+        b7 = b3;
+    } else {
+        a0 = c.wm + r0 * K + sa * 32;
+        a1 = a0 + 16;
+        a2 = c.wm + r1 * K + sa * 32;
+        a3 = a2 + 16;
+        b0 = c.wm + c.o1 + (r0 * nsub + sa) * 2;
+        b1 = c.wm + c.o1 + (r1 * nsub + sa) * 2;
+        b2 = b0;
+        b3 = b1;
+        b4 = b0;
+        b5 = b1;
+        b6 = b0;
+        b7 = b1;
+    }
+    s.q0 = q16(a0);
+    s.q1 = q16(a1);
+    s.q2 = q16(a2);
+    s.q3 = q16(a3);
+    s.h0 = h2(b0);
+    s.h1 = h2(b1);
+    s.h2 = h2(b2);
+    s.h3 = h2(b3);
+    s.h4 = h2(b4);
+    s.h5 = h2(b5);
+    s.h6 = h2(b6);
+    s.h7 = h2(b7);
+}
+
+// The block terms of one step (sub-block sl of the staged chunk) for the
+// two rows whose records are I0 and I0 + 1 of the slot, into acc[p][*].
+template <int QT, int I0, int M>
+__device__ __forceinline__ void step_terms(const Slot &s, const ActLds &A, int sl, float (&acc)[2][M]) {
+    const int jl = threadIdx.x & 7;
+    WDec d0, d1;
+    decode_w<QT>(d0, rec_of<QT, I0>(s), jl);
+    decode_w<QT>(d1, rec_of<QT, I0 + 1>(s), jl);
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        ARec ar;
+        read_act(ar, A, m, sl);
+        const AExt ae = act_ext(ar);
+        acc[0][m] = block_term<QT>(d0, ar, ae, acc[0][m]);
+        acc[1][m] = block_term<QT>(d1, ar, ae, acc[1][m]);
+    }
+}
+
+// Dot products of the item in slot s into acc[row][position].
+template <int M>
+__device__ __forceinline__ void consume(const Slot &s, const ItemCur &c, const ActLds &A, float (&acc)[2][M]) {
+    const int jl = threadIdx.x & 7;
+    const int64_t nsub = c.K >> 5;
+    if (c.qtype == SV_Q4_K) {
+        const int t = c.s.w0 + c.item * 2;
+        if (t < c.s.w1) step_terms<SV_Q4_K, 0, M>(s, A, t * 8 + jl - c.g.s_begin, acc);
+        if (t + 1 < c.s.w1) step_terms<SV_Q4_K, 2, M>(s, A, (t + 1) * 8 + jl - c.g.s_begin, acc);
+    } else {
+        const int t = c.s.w0 + c.item;
+        const int64_t sb = static_cast<int64_t>(t) * 8 + jl;
+        if (t < c.s.w1 && sb < nsub) {
+            const int sl = static_cast<int>(sb) - c.g.s_begin;
+            if (c.qtype == SV_Q6_K) step_terms<SV_Q6_K, 0, M>(s, A, sl, acc);
+            else step_terms<SV_Q8_0, 0, M>(s, A, sl, acc);
+        }
+    }
+}
+
+// End of a unit: the fixed-order sum of each row group's 8 lanes, written
+// to the wave's partial slots [wave][position][row of the half tile].
+template <int M>
+__device__ __forceinline__ void put_partials(float *wp, float (&acc)[2][M]) {
+    const int lane = threadIdx.x & 63;
+    const int wave = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    const int grp = lane >> 3, jl = lane & 7;
+#pragma unroll
+    for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float v = group8_sum(acc[p][m]);
+            if (jl == 0) wp[(wave * M + m) * 16 + grp * 2 + p] = v;
+            acc[p][m] = 0.0f;
+        }
+}
+
+// State of a compute wave between ring items.
+template <int M>
+struct CompState {
+    ItemCur L, C;     // load cursor (a ring ahead) and compute cursor
+    bool lv, go;      // load cursor not yet past the end; compute cursor valid and no abort
+    int buf;          // wave-partial buffer of the current unit
+    ActLds A;
+    float acc[2][M];
+};
+
+// One ring step: consume the item in slot s (if the compute cursor is
+// still valid), refill s with the item the load cursor points at, and close
+// the unit if this was its last item.  The refill is issued on every step:
+// a load cursor past the workgroup's last item reads that item again, so
+// the loads in flight never depend on the path taken.
+template <int M, class Tab>
+__device__ __forceinline__ void ring_step(const Tab &tab, int n_phases, uint32_t b, uint32_t G, int wave,
+                                          uint8_t *smem, Shared<M> &sh, CompState<M> &st, Slot &s) {
+    if (st.go && st.C.item == 0 && st.C.sync) {
+        lds_barrier();   // B1: the unit's input is staged
+        if (sh.abort) st.go = false;
+        else st.A = act_lds(act_base<M>(smem), M, st.C.g.cs);
+    }
+    if (st.go) consume<M>(s, st.C, st.A, st.acc);
+    load_item(s, st.L);
+    if (st.lv) st.lv = cur_advance_keep(tab, n_phases, b, G, st.L, wave, true);
+    if (st.go && st.C.item == st.C.s.nitems - 1) {
+        put_partials<M>(wpart_buf<M>(smem, st.buf), st.acc);
+        lds_barrier();   // B2: the unit's partial sums are written
+        st.buf ^= 1;
+        if (sh.abort) st.go = false;
+    }
+    if (st.go) st.go = cur_advance(tab, n_phases, b, G, st.C, wave, false);
+}
+
+template <int M, class Tab>
+__device__ __forceinline__ void prime(const Tab &tab, int n_phases, uint32_t b, uint32_t G, int wave,
+                                      CompState<M> &st, Slot &s) {
+    load_item(s, st.L);
+    if (st.lv) st.lv = cur_advance_keep(tab, n_phases, b, G, st.L, wave, true);
+}
+
+template <int M, class Tab>
+__device__ __forceinline__ void compute_waves(const Tab &tab, int n_phases, uint32_t b, uint32_t G, uint8_t *smem,
+                                              Shared<M> &sh) {
+    constexpr int D = RingDepth<M>::value;
+    const int wave = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
+    CompState<M> st;
+    st.lv = cur_init(tab, n_phases, b, G, st.L, wave, true);
+    st.go = cur_init(tab, n_phases, b, G, st.C, wave, false);
+    if (!st.go) return;
+    st.buf = 0;
+#pragma unroll
+    for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int m = 0; m < M; m++) st.acc[p][m] = 0.0f;
+    // separate slots (no array): every access has a constant address from
+    // the start, so the slots live in registers
+    Slot s0, s1, s2, s3;
+    prime<M>(tab, n_phases, b, G, wave, st, s0);
+    prime<M>(tab, n_phases, b, G, wave, st, s1);
+    if constexpr (D > 2) prime<M>(tab, n_phases, b, G, wave, st, s2);
+    if constexpr (D > 3) prime<M>(tab, n_phases, b, G, wave, st, s3);
+    while (st.go) {
+        ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s0);
+        ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s1);
+        if constexpr (D > 2) ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s2);
+        if constexpr (D > 3) ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s3);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// ============================================================ control wave
+__device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target, unsigned *status) {
+    const int lane = threadIdx.x & 63;
+    unsigned n = 0;
+    // two polls in flight: the next read is issued before the previous one
+    // is examined, so an update is seen about half a round trip sooner
+    // every lane reads (lanes >= kSlots repeat the first slots), so no
+    // branch hides the loads from the wait-count bookkeeping
+    const int rep = static_cast<int>(blockIdx.x % kReplicas);
+    const unsigned *slot = ctr + (rep * kSlots + (lane & (kSlots - 1))) * kSlotStride;
+    unsigned a = ld_dev(slot);
+    for (;;) {
+        __builtin_amdgcn_s_sleep(2);
+        const unsigned bb = ld_dev(slot);
+        unsigned v = (lane < kSlots) ? a : 0u;
+#pragma unroll
+        for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+        v = __shfl(v, 0, 64);
+        if (v >= target) return true;
+        if (++n > kSpinLimit || ((n & 63u) == 0u && ld_dev(status) != 0u)) {
+            if (lane == 0) or_dev(status, 1u);
+            return false;
+        }
+        a = bb;
+    }
+}
+
+// Copies the input chunk of a phase (codes, scales, code sums and, if the
+// input is RMS-normalised, its partials) into LDS with load-to-LDS
+// transfers, then forms the RMS factors: lane l adds partials l, l + 64,
+// ... in order, then wave_sum (a fixed order that depends only on the
+// number of partials).
+template <int M, class PD>
+__device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *act, Shared<M> &sh) {
+    const int lane = threadIdx.x & 63;
+    const int K = P.K, nsub = K >> 5, cs = g.cs;
+    const int8_t *aq = P.aq;
+    const float *ad = P.ad;
+    const int32_t *as16 = P.as16;
+    const float *parts = P.in_parts;
+    const int n_parts = P.n_parts;
+    uint8_t *qd = act;
+    float *dd = reinterpret_cast<float *>(act + M * cs * 32);
+    int32_t *xd = reinterpret_cast<int32_t *>(act + M * cs * 36);
+    float *pd = reinterpret_cast<float *>(act + M * cs * 44);
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(aq) + static_cast<int64_t>(m) * K +
+                             static_cast<int64_t>(g.s_begin) * 32;
+        const int n16 = cs * 2;
+        for (int k = 0; 64 * k < n16; k++) {
+            const int i = 64 * k + lane;
+            if (i < n16)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + i * 16),
+                                                 (SV_AS3 void *)(qd + m * cs * 32 + 64 * k * 16), 16, 0, 0);
+        }
+        const float *dsrc = ad + static_cast<int64_t>(m) * nsub + g.s_begin;
+        for (int k = 0; 64 * k < cs; k++) {
+            const int i = 64 * k + lane;
+            if (i < cs)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(dsrc + i),
+                                                 (SV_AS3 void *)(dd + m * cs + 64 * k), 4, 0, 0);
+        }
+        const int32_t *xsrc = as16 + static_cast<int64_t>(m) * (K >> 4) + 2 * g.s_begin;
+        for (int k = 0; 64 * k < 2 * cs; k++) {
+            const int i = 64 * k + lane;
+            if (i < 2 * cs)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(xsrc + i),
+                                                 (SV_AS3 void *)(xd + m * 2 * cs + 64 * k), 4, 0, 0);
+        }
+    }
+    if (parts) {
+        const int total = M * n_parts;
+        for (int k = 0; 64 * k < total; k++) {
+            const int f = 64 * k + lane;
+            if (f < total)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(parts + f),
+                                                 (SV_AS3 void *)(pd + 64 * k), 4, 0, 0);
+        }
+    }
+    // the transfers have written LDS once this wave's loads are complete
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int m = 0; m < M; m++) {
+        float r = 1.0f;
+        if (parts) {
+            float t = 0.0f;
+            for (int i = lane; i < n_parts; i += 64) t += pd[m * n_parts + i];
+            const float tot = wave_sum(t);
+            r = 1.0f / sqrtf(tot / static_cast<float>(K) + P.eps);
+        }
+        if (lane == 0) sh.rscale[m] = r;
+    }
+}
+
+// Adds the workgroup's best (logit, index) keys of the phase to its argmax
+// words.  In a pass those words are cleared by workgroup 0 at launch, so the
+// control wave waits for the flag that says so (set within microseconds of
+// the start, long before any head tile is done; bounded like every wait)
+// before its first atomic maximum.
+template <int M>
+__device__ __forceinline__ void flush_best(unsigned long long *argmax, Shared<M> &sh, const unsigned *cleared,
+                                           unsigned *status) {
+    const int lane = threadIdx.x & 63;
+    if (!argmax) return;
+    if (cleared) {
+        unsigned n = 0;
+        while (ld_dev(cleared) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++n > kSpinLimit) {
+                if (lane == 0) or_dev(status, 2u);
+                break;
+            }
+        }
+    }
+    if (lane < M) {
+        const unsigned long long v = sh.best[lane];
+        if (v) max_dev(argmax + lane, v);
+        sh.best[lane] = 0ull;
+    }
+}
+
+// Values of a finished row tile in the control wave: lane l holds row
+// r = l & 31 at positions m = (l >> 5) + 2k.
+template <int M>
+struct TileVals {
+    float v[(M + 1) / 2];
+};
+
+template <int M, class PD>
+__device__ __forceinline__ void store_y(const PD &P, int mt, int64_t row0, const TileVals<M> &x) {
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+    const int64_t N = P.N;
+    float *y = P.y[mt];
+    if (!y) return;
+    const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), N - row0));
+#pragma unroll
+    for (int k = 0; k < (M + 1) / 2; k++) {
+        const int m = h + 2 * k;
+        if (m < M && r < rows_here) gst(y + static_cast<int64_t>(m) * N + row0 + r, x.v[k]);
+    }
+}
+
+// Argmax candidates (the head's values x) and the requantised next
+// activation from e (the epilogue's source: y[ep_src], or g*u for a pair):
+// amax, d, codes, 16-element code sums and the sum of squares of each
+// 32-row block, i.e. of one activation block.
+template <int M, class PD>
+__device__ __forceinline__ void finish_tile(const PD &P, int64_t row0, const TileVals<M> &x, const TileVals<M> &e,
+                                            bool do_ep, Shared<M> &sh) {
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+    const int64_t N = P.N;
+    const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), N - row0));
+    unsigned long long *am = P.argmax;
+    if (am) {
+#pragma unroll
+        for (int k = 0; k < (M + 1) / 2; k++) {
+            const int m = h + 2 * k;
             const unsigned long long key =
-                l32 < rows_here ? pack_argmax(ystage[m * kRows + l32], static_cast<uint32_t>(row0 + l32)) : 0ull;
-            const unsigned long long b = half_max64(key);
-            if (l32 == 0 && b) atomicMax(&sh.best[m], b);
+                r < rows_here ? pack_argmax(x.v[k], static_cast<uint32_t>(row0 + r)) : 0ull;
+            const unsigned long long bk = half_max64(key);
+            if (m < M && r == 0 && bk > sh.best[m]) sh.best[m] = bk;
         }
     }
     if (do_ep && P.ep_mode != SV_EP_NONE && rows_here == kRows) {
-        const int64_t N = P.N;
-        for (int m = hw; m < M; m += kThreads / 32) {
-            float v;
-            if (P.ep_mode == SV_EP_PAIR) v = ystage[(0 * M + m) * kRows + l32] * ystage[(1 * M + m) * kRows + l32];
-            else v = ystage[(P.ep_src * M + m) * kRows + l32];
-            const int64_t grow = row0 + l32;
-            const float vg = P.gamma ? v * g_row : v;
-            const float am = half_max(fabsf(vg));
-            const float dd = am / 127.0f;
+        const float *gamma = P.gamma;
+        const float g_row = gamma ? gld(gamma + row0 + r) : 1.0f;
+        int8_t *oq = P.oq;
+        float *od = P.od, *osumsq = P.osumsq;
+        int32_t *os16 = P.os16;
+        const int64_t gb = row0 >> 5;
+#pragma unroll
+        for (int k = 0; k < (M + 1) / 2; k++) {
+            const int m = h + 2 * k;
+            const float v = e.v[k];
+            const float vg = gamma ? v * g_row : v;
+            const float amx = half_max(fabsf(vg));
+            const float dd = amx / 127.0f;
             const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
             float rq = roundf(vg * id);
             rq = fminf(fmaxf(rq, -127.0f), 127.0f);
             const int qi = static_cast<int>(rq);
             const int s = row_sum(qi);
             const float sq = half_sum(v * v);
-            st_dev(P.oq + m * N + grow, static_cast<int8_t>(qi));
-            const int64_t gb = grow >> 5;
-            if ((l32 & 15) == 0) st_dev(P.os16 + m * (N >> 4) + 2 * gb + (l32 >> 4), s);
-            if (l32 == 0) {
-                st_dev(P.od + m * (N >> 5) + gb, dd);
-                st_dev(P.osumsq + m * (N >> 5) + gb, sq);
+            if (m < M) {
+                st_dev(oq + m * N + row0 + r, static_cast<int8_t>(qi));
+                if ((r & 15) == 0) st_dev(os16 + m * (N >> 4) + 2 * gb + (r >> 4), s);
+                if (r == 0) {
+                    st_dev(od + m * (N >> 5) + gb, dd);
+                    st_dev(osumsq + m * (N >> 5) + gb, sq);
+                }
             }
         }
     }
 }
 
-// Positions staged in LDS at once (two rounds for M > 8; the raw weights
-// stay in registers, so nothing is read twice from memory).
-template <int M>
-struct MG {
-    static constexpr int value = M > 8 ? 8 : M;
-};
-
-// The rows, K chunk and matrix of a unit under the R-rows-per-lane layout:
-// wave w takes rows [rw, rw + 32 / RS), rw = row0 + (32 / RS) (w % RS),
-// over steps [w0, w1), the (w / RS)-th of SS parts of the chunk's steps.
-struct UnitGeom {
-    int tile, chunk, mat, c0, w0, w1, cs;
-    int64_t row0, rw, s_begin;
-};
-
-template <int R>
-__device__ __forceinline__ UnitGeom unit_geom(const PhaseDesc &P, int unit) {
-    constexpr int RS = 4 / R, SS = 4 / RS;
-    UnitGeom g;
-    const int wave = threadIdx.x >> 6;
-    g.tile = unit / P.per_tile;
-    const int rem = unit % P.per_tile;
-    g.chunk = rem % P.S;
-    g.mat = rem / P.S;
-    g.row0 = static_cast<int64_t>(g.tile) * kRows;
-    const int64_t nsub = P.K >> 5;
-    g.c0 = static_cast<int>(static_cast<int64_t>(g.chunk) * P.steps / P.S);
-    const int c1 = static_cast<int>(static_cast<int64_t>(g.chunk + 1) * P.steps / P.S);
-    const int tc = c1 - g.c0;
-    g.w0 = g.c0 + (wave / RS) * tc / SS;
-    g.w1 = g.c0 + (wave / RS + 1) * tc / SS;
-    g.rw = g.row0 + (kRows / RS) * (wave % RS);
-    g.s_begin = static_cast<int64_t>(g.c0) * 8;
-    g.cs = static_cast<int>(min(static_cast<int64_t>(tc) * 8, nsub - g.s_begin));
-    return g;
-}
-
-// Request every weight record of a unit (at most WS steps per
-// wave and matrix) into raw.
-// ALL: every record is written (steps a wave does not take re-read a
-// record of its chunk), so no value of an earlier unit has to be kept.
-template <int QT, int NM, bool ALL = false, int WS, int R>
-__device__ __forceinline__ void issue_weights(WRaw<QT> (&raw)[NM][WS][R], const PhaseDesc &P,
-                                              const UnitGeom &g) {
-    const int lane = threadIdx.x & 63;
-    const int grp = lane >> 3, jl = lane & 7;
-    const int64_t nsub = P.K >> 5;
-    int64_t srow[R];
-#pragma unroll
-    for (int p = 0; p < R; p++) {
-        int64_t rr = g.rw + grp * R + p;
-        if (rr >= P.N) rr = 0;
-        const int64_t sr = P.row_ids ? static_cast<int64_t>(gld(P.row_ids + rr)) : rr;
-        // out-of-range ids are a caller error; clamp so no read leaves the matrix
-        srow[p] = (sr < 0 || sr >= P.wrows) ? 0 : sr;
-    }
-#pragma unroll
-    for (int mm = 0; mm < NM; mm++) {
-        const uint8_t *__restrict__ w = P.w[g.mat + mm];
-#pragma unroll
-        for (int t = 0; t < WS; t++) {
-            const int64_t sb = static_cast<int64_t>(g.w0 + t) * 8 + jl;
-            if (ALL) {
-                const int64_t sc = (g.w0 + t < g.w1 && sb < nsub) ? sb : static_cast<int64_t>(g.c0) * 8;
-#pragma unroll
-                for (int p = 0; p < R; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sc);
-            } else if (g.w0 + t < g.w1 && sb < nsub) {
-#pragma unroll
-                for (int p = 0; p < R; p++) load_w<QT>(raw[mm][t][p], w, P, srow[p], sb);
-            }
-        }
-    }
-}
-
-// One unit: rows [row0, row0 + 32) x the K chunk `chunk`, for NM matrices
-// from `mat` (NM = 2: both matrices of a gate/up pair, so the pair's
-// product forms inside the unit).  Wave w takes rows [rw, rw + 32 / RS)
-// over steps [w0, w1) of the chunk of each matrix (one step = 8 sub-blocks
-// per row, one 256-element super-block of a K-quant); lane j of row group
-// grp reads sub-block 8 t + j of rows rw + R grp + p, p < R.
-// OWN: the unit requests its own weights first (raw is scratch); else raw
-// already holds them (software-pipelined phases) and next >= 0 names the
-// unit whose weights to request once the dot products are done.
-template <int QT, int M, int NM, bool OWN>
-__device__ __forceinline__ bool run_unit(const PhaseDesc &P, int unit,
-                                         WRaw<QT> (&raw_in)[NM][Lay::WS][Lay::R],
-                                         int next, uint8_t *act, float *ystage, float *wpart, float *parts, int CS,
-                                         Shared<M> &sh, bool do_wait, bool timed, unsigned *status, bool restage) {
-    constexpr int MGV = MG<M>::value;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int grp = lane >> 3, jl = lane & 7;
+// The control wave's part of a unit whose partial sums sit in wave-partial
+// buffer wp: adds the four step quarters of each row in order, then either
+// finishes the tile, or (K split over units, or one matrix of a gate/up
+// pair) stores the chunk's values, and the last unit of the tile to arrive
+// adds all chunks in chunk order (and forms g * u) and finishes it.  Then the unit is
+// handed off if a later phase reads it.
+template <int M, class PD>
+__device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float *wp, Shared<M> &sh) {
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5, hr = r >> 4, rr = r & 15;
+    const UnitPos g = unit_pos(P, u);
+    const int64_t row0 = static_cast<int64_t>(g.tile) * kRows;
+    const int64_t N = P.N;
     const bool pair = P.ep_mode == SV_EP_PAIR;
-    const int per_tile = P.per_tile;
-    constexpr int kR = Lay::R, RS = Lay::RS, SS = Lay::SS, WS = Lay::WS;
-    const UnitGeom g = unit_geom<kR>(P, unit);
-    const int tile = g.tile, chunk = g.chunk, mat = g.mat;
-    const int64_t row0 = g.row0;
-    const int64_t nsub = P.K >> 5;
-    const int w0 = g.w0, w1 = g.w1;
-    const int64_t s_begin = g.s_begin;
-    const int cs = g.cs;
-    WRaw<QT> raw_own[NM][WS][kR];
-    WRaw<QT>(&raw)[NM][WS][kR] = OWN ? raw_own : raw_in;
-    if (OWN) issue_weights<QT, NM>(raw, P, g);
-    // the epilogue's norm weight of this thread's row, fetched off the
-    // critical path
-    float g_row = 1.0f;
-    if (P.gamma && P.ep_mode != SV_EP_NONE) {
-        const int64_t gr = row0 + (threadIdx.x & 31);
-        if (gr < P.N) g_row = gld(P.gamma + gr);
+    const bool split = P.S > 1 || pair;
+    // the step quarters of each row, added in order: waves hr, hr + 2, ...
+    TileVals<M> v0;
+#pragma unroll
+    for (int k = 0; k < (M + 1) / 2; k++) {
+        const int m = min(h + 2 * k, M - 1);
+        float v = wp[(hr * M + m) * 16 + rr];
+#pragma unroll
+        for (int q = 1; q < kStepParts; q++) v += wp[((hr + 2 * q) * M + m) * 16 + rr];
+        v0.v[k] = v;
     }
-    bool need_rs = false;
-    if (do_wait) {
-        if (P.wait && !wait_ready(P.wait, P.wait_target, status, sh.abort)) return false;
-        if (timed && threadIdx.x == 0) {
-            sh.t_wait = __builtin_amdgcn_s_memrealtime();
-            sh.t_reduced = 0ull;
-            sh.t_epi = 0ull;
+    if (!split) {
+#pragma unroll
+        for (int k = 0; k < (M + 1) / 2; k++) v0.v[k] *= sh.rscale[min(h + 2 * k, M - 1)];
+        store_y<M>(P, g.mat, row0, v0);
+        finish_tile<M>(P, row0, v0, v0, g.mat == P.ep_src, sh);
+    } else {
+        float *partial = P.partial;
+        const int S = P.S;
+#pragma unroll
+        for (int k = 0; k < (M + 1) / 2; k++) {
+            const int m = h + 2 * k;
+            if (m < M && row0 + r < N)
+                st_dev(partial + ((static_cast<int64_t>(g.mat) * S + g.chunk) * M + m) * N + row0 + r, v0.v[k]);
         }
-        need_rs = true;
-    }
-    float acc[NM][kR][M];
+        drain();
+        unsigned *tc = P.tile_count;
+        unsigned prev = 0;
+        if (lane == 0) prev = add_dev(tc + g.tile, 1u);
+        prev = static_cast<unsigned>(__shfl(static_cast<int>(prev), 0, 64));
+        if (prev == static_cast<unsigned>(P.per_tile - 1)) {
+            const int n_w = P.n_w, src = P.ep_src;
+            TileVals<M> f0, e;
 #pragma unroll
-    for (int mm = 0; mm < NM; mm++)
+            for (int mt = 0; mt < 3; mt++) {
+                if (mt < n_w) {
+                    TileVals<M> f;
 #pragma unroll
-        for (int p = 0; p < kR; p++)
+                    for (int k = 0; k < (M + 1) / 2; k++) {
+                        const int m = h + 2 * k;
+                        float s = 0.0f;
+                        if (m < M && row0 + r < N) {
+                            const float *srcp = partial + (static_cast<int64_t>(mt) * S * M + m) * N + row0 + r;
+                            float v[kMaxS];
 #pragma unroll
-            for (int m = 0; m < M; m++) acc[mm][p][m] = 0.0f;
+                            for (int c = 0; c < kMaxS; c++) {
+                                // every chunk's partial is requested before any is used
+                                const float xx = ld_dev(srcp + static_cast<int64_t>(c < S ? c : 0) * M * N);
+                                v[c] = c < S ? xx : 0.0f;
+                            }
 #pragma unroll
-    for (int m0 = 0; m0 < M; m0 += MGV) {
-        const int mg = min(MGV, M - m0);
-        // the chunk staged for the previous unit of this phase may be the
-        // same one (then it is still in LDS)
-        if (restage || M > MGV) {
-            lds_barrier();
-            if (m0 == 0 && need_rs && P.in_parts) rms_fetch(parts, P, M);
-            stage_act(act, P, m0, mg, s_begin, cs, CS);
-            // LDS transfers of this wave are complete once its loads are
-            __builtin_amdgcn_s_waitcnt(0);
-            lds_barrier();
-        }
-        if (timed && m0 == 0 && threadIdx.x == 0) sh.t_staged = __builtin_amdgcn_s_memrealtime();
-#pragma unroll
-        for (int t = 0; t < WS; t++) {
-            const int64_t sb = static_cast<int64_t>(w0 + t) * 8 + jl;
-            if (w0 + t < w1 && sb < nsub) {
-                const int sl = static_cast<int>(sb - s_begin);
-#pragma unroll
-                for (int mm = 0; mm < NM; mm++) {
-                    WDec dec[kR];
-#pragma unroll
-                    for (int p = 0; p < kR; p++) decode_w<QT>(dec[p], raw[mm][t][p], jl);
-#pragma unroll
-                    for (int m = 0; m < MGV; m++) {
-                        if (m0 + m < M) {
-                            ARec ar;
-                            read_act(ar, act + m * CS * kActRec, CS, sl);
-                            const AExt ae = act_ext<QT>(ar);
-#pragma unroll
-                            for (int p = 0; p < kR; p++)
-                                acc[mm][p][m0 + m] = block_term<QT>(dec[p], ar, ae, acc[mm][p][m0 + m]);
+                            for (int c = 0; c < kMaxS; c++)
+                                if (c < S) s += v[c];
                         }
+                        f.v[k] = s * sh.rscale[min(m, M - 1)];
+                    }
+                    store_y<M>(P, mt, row0, f);
+                    if (mt == 0) {
+                        f0 = f;
+                        e = f;
+                    } else if (pair && mt == 1) {
+#pragma unroll
+                        for (int k = 0; k < (M + 1) / 2; k++) e.v[k] = f0.v[k] * f.v[k];
+                    } else if (!pair && mt == src) {
+                        e = f;
                     }
                 }
             }
+            if (lane == 0) st_dev(tc + g.tile, 0u);
+            finish_tile<M>(P, row0, f0, e, true, sh);
         }
     }
-    if (timed && threadIdx.x == 0) sh.t_computed = __builtin_amdgcn_s_memrealtime();
-    // The weight registers are free: the next unit's records are requested
-    // now, so they stream in during this unit's reduction and epilogue.
-    if (!OWN && next >= 0) issue_weights<QT, NM, true>(raw, P, unit_geom<kR>(P, next));
-    // The input's RMS factors (first unit of a phase) are formed now, with
-    // the weight registers free: their loads are in flight during the
-    // reduction below.
-    const bool rms = need_rs && P.in_parts;
-    // Lanes of a row group: fixed-order sum; waves: partials through LDS,
-    // added in wave order.
-#pragma unroll
-    for (int mm = 0; mm < NM; mm++)
-#pragma unroll
-        for (int p = 0; p < kR; p++)
-#pragma unroll
-            for (int m = 0; m < M; m++) {
-                const float v = group8_sum(acc[mm][p][m]);
-                if (jl == 0)
-                    wpart[((wave * NM + mm) * M + m) * kRows + (kRows / RS) * (wave % RS) + grp * kR + p] = v;
-            }
-    if (rms) {
-        rms_store(parts, P, M, sh.rscale);
-    } else if (need_rs && threadIdx.x < M) {
-        sh.rscale[threadIdx.x] = 1.0f;
+    // hand-off: only units a later phase reads are counted
+    unsigned *ready = P.ready;
+    if (ready && (P.count_all || g.mat == P.ep_src)) {
+        drain();
+        if (lane < kReplicas) add_dev(ready + (lane * kSlots + u % kSlots) * kSlotStride, 1u);
     }
-    lds_barrier();
-    // chunk value of (m, row): the SS step parts added in order, from waves
-    // rs, rs + RS, ... of the row's part rs.  A tile is final here unless K
-    // is split over units or a pair's matrices sit in two units.
-    const bool split = P.S > 1 || (pair && NM == 1);
-    for (int i = threadIdx.x; i < NM * M * kRows; i += kThreads) {
-        const int mm = i / (M * kRows), r2 = i % (M * kRows), m = r2 / kRows, r = r2 % kRows;
-        const int rs = r / (kRows / RS);
-        float v = wpart[((rs * NM + mm) * M + m) * kRows + r];
-#pragma unroll
-        for (int sp = 1; sp < SS; sp++) v += wpart[(((sp * RS + rs) * NM + mm) * M + m) * kRows + r];
-        if (!split) {
-            ystage[((mat + mm) * M + m) * kRows + r] = v * sh.rscale[m];
-        } else {
-            const int64_t rr = row0 + r;
-            if (rr < P.N)
-                st_dev(P.partial + ((static_cast<int64_t>(mat + mm) * P.S + chunk) * M + m) * P.N + rr, v);
-        }
-    }
-    if (!split) {
-        lds_barrier();
-        if (timed && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
-        finish_tile<M>(P, ystage, row0, mat, mat + NM, NM == 2 || mat == P.ep_src, g_row, sh);
-        if (timed && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
-        return true;
-    }
-    // K split over units: the last unit of the tile to finish adds the chunk
-    // partials in chunk order and runs the epilogue.
-    drain();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = add_dev(P.tile_count + tile, 1u);
-        sh.last = (prev == static_cast<unsigned>(per_tile - 1)) ? 1 : 0;
-    }
-    lds_barrier();
-    if (!sh.last) return true;
-    const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), static_cast<int64_t>(P.N) - row0));
-    for (int i = threadIdx.x; i < P.n_w * M * kRows; i += kThreads) {
-        const int mt = i / (M * kRows), r2 = i % (M * kRows), m = r2 / kRows, r = r2 % kRows;
-        float s = 0.0f;
-        if (r < rows_here) {
-            const float *src = P.partial + (static_cast<int64_t>(mt) * P.S * M + m) * P.N + row0 + r;
-            float v[kMaxS];
-#pragma unroll
-            for (int c = 0; c < kMaxS; c++) {
-                // every chunk's partial is requested before any is used
-                const float x = ld_dev(src + static_cast<int64_t>(c < P.S ? c : 0) * M * P.N);
-                v[c] = c < P.S ? x : 0.0f;
-            }
-#pragma unroll
-            for (int c = 0; c < kMaxS; c++)
-                if (c < P.S) s += v[c];
-        }
-        ystage[(mt * M + m) * kRows + r] = s * sh.rscale[m];
-    }
-    if (threadIdx.x == 0)
-        st_dev(P.tile_count + tile, 0u);
-    lds_barrier();
-    if (timed && threadIdx.x == 0) sh.t_reduced = __builtin_amdgcn_s_memrealtime();
-    finish_tile<M>(P, ystage, row0, 0, P.n_w, true, g_row, sh);
-    if (timed && threadIdx.x == 0) sh.t_epi = __builtin_amdgcn_s_memrealtime();
-    return true;
 }
 
-
-// The units u, u + G, ... < nu of one phase on this workgroup.  A unit whose
-// output the next phase reads is drained and counted; any other unit lets
-// the next one's weights stream in during its own reduction and epilogue.
-template <int QT, int M, int NM, bool PF>
-__device__ __forceinline__ bool run_phase(const PhaseDesc &P, uint32_t u, uint32_t G, uint32_t nu, uint8_t *act,
-                                          float *ystage, float *wpart, float *parts, int CS, Shared<M> &sh,
-                                          unsigned *status, unsigned long long *tr) {
-    WRaw<QT> raw[NM][Lay::WS][Lay::R];
-    if (PF) issue_weights<QT, NM, true>(raw, P, unit_geom<Lay::R>(P, static_cast<int>(u)));
-    bool first = true;
-    int staged = -1;   // first step of the K chunk in LDS
-    unsigned n_done = 0;
-    for (; u < nu; u += G) {
-        const int rem = static_cast<int>(u % P.per_tile);
-        const int chunk = rem % P.S;
-        const int c0 = static_cast<int>(static_cast<int64_t>(chunk) * P.steps / P.S);
-        // Only units whose outputs the next phase reads are handed off
-        // (drained and counted); the last phase has no reader at all.
-        const bool counted = P.ready && (P.count_all || rem / P.S == P.ep_src);
-        const bool more = u + G < nu;
-        const int next = (PF && more && !counted) ? static_cast<int>(u + G) : -1;
-        if (!run_unit<QT, M, NM, !PF>(P, static_cast<int>(u), raw, next, act, ystage, wpart, parts, CS, sh, first,
-                                      first && tr != nullptr, status, c0 != staged))
-            return false;
-        staged = c0;
-        n_done++;
-        if (counted) drain();
-        lds_barrier();
-        if (counted && threadIdx.x < kReplicas)
-            add_dev(P.ready + (threadIdx.x * kSlots + u % kSlots) * kSlotStride, 1u);
-        if (threadIdx.x == 0) {
-            sh.last = 0;
-            if (first && tr) {
-                tr[1] = sh.t_wait;
-                tr[2] = sh.t_staged;
-                tr[3] = sh.t_computed;
-                tr[4] = __builtin_amdgcn_s_memrealtime();
-                tr[7] = sh.t_reduced;
-                tr[8] = sh.t_epi;
+template <int M, class Tab>
+__device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint32_t b, uint32_t G, uint8_t *smem,
+                                             Shared<M> &sh, unsigned *status, const unsigned *cleared,
+                                             unsigned long long *trace) {
+    const int lane = threadIdx.x & 63;
+    UnitCur c;
+    unit_first(tab, n_phases, b, G, c);
+    int pp = -1, pchunk = -1, buf = 0;
+    uint32_t pu = 0;
+    // what is staged: the input codes, the chunk and the partials
+    const int8_t *st_q = nullptr;
+    const float *st_parts = nullptr;
+    int st_begin = -1, st_cs = -1;
+    unsigned long long *tr = nullptr;
+    unsigned n_units = 0;
+    uint8_t *act = act_base<M>(smem);
+    while (c.p < n_phases) {
+        const auto &P = tab[c.p];
+        const UnitPos g = unit_pos(P, c.u);
+        if (pp >= 0) {
+            ctrl_finish<M>(tab[pp], pu, wpart_buf<M>(smem, buf ^ 1), sh);
+            if (tr && lane == 0) {
+                if (n_units == 1) tr[4] = now();
+                tr[5] = now();
             }
         }
-        first = false;
-        lds_barrier();
-        if (PF && more && next < 0)
-            issue_weights<QT, NM, true>(raw, P, unit_geom<Lay::R>(P, static_cast<int>(u + G)));
-    }
-    if (tr && threadIdx.x == 0) {
-        tr[5] = __builtin_amdgcn_s_memrealtime();
-        tr[6] = n_done;
-    }
-    return true;
-}
-
-template <int M>
-__device__ __forceinline__ bool dispatch_phase(const PhaseDesc &P, uint32_t u, uint32_t G, uint32_t nu, uint8_t *act,
-                                               float *ystage, float *wpart, float *parts, int CS, Shared<M> &sh,
-                                               unsigned *status, unsigned long long *tr) {
-    // Phases with several units per workgroup and no reader (the head) run
-    // software-pipelined: each unit's successor streams in during its
-    // reduction and epilogue.
-    if (!P.ready && u + G < nu) {
-        if (P.qtype == SV_Q6_K)
-            return run_phase<SV_Q6_K, M, 1, true>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
-        if (P.qtype == SV_Q8_0)
-            return run_phase<SV_Q8_0, M, 1, true>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
-    }
-    if (P.qtype == SV_Q4_K) {
-        if (P.fused) return run_phase<SV_Q4_K, M, 2, false>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
-        return run_phase<SV_Q4_K, M, 1, false>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
-    }
-    if (P.qtype == SV_Q6_K)
-        return run_phase<SV_Q6_K, M, 1, false>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
-    return run_phase<SV_Q8_0, M, 1, false>(P, u, G, nu, act, ystage, wpart, parts, CS, sh, status, tr);
-}
-
-// Adds the workgroup's best (logit, index) keys of the phase to its argmax
-// words.  In a pass those words are cleared by workgroup 0 at launch, so a
-// workgroup waits for the flag that says so (set within microseconds of the
-// start, long before any head tile is done; the wait is bounded like every
-// other) before its first atomic maximum.
-__device__ __forceinline__ void flush_best(const PhaseDesc &P, unsigned long long *best, int M,
-                                           const unsigned *cleared, unsigned *status) {
-    __syncthreads();
-    if (P.argmax && static_cast<int>(threadIdx.x) < M) {
-        if (cleared) {
-            unsigned n = 0;
-            while (ld_dev(cleared) == 0u) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++n > kSpinLimit) {
-                    or_dev(status, 2u);
-                    break;
+        const bool phase_change = c.p != pp;
+        if (phase_change || g.chunk != pchunk) {
+            if (phase_change && pp >= 0) flush_best<M>(tab[pp].argmax, sh, cleared, status);
+            if (phase_change) {
+                if (tr && lane == 0) tr[6] = n_units;
+                tr = trace ? trace + (static_cast<size_t>(b) * n_phases + c.p) * kTraceWords : nullptr;
+                n_units = 0;
+                if (tr && lane == 0) {
+                    tr[0] = now();
+                    tr[9] = static_cast<unsigned long long>(__builtin_amdgcn_s_getreg(0xF804)) |
+                            (static_cast<unsigned long long>(__builtin_amdgcn_s_getreg(0xF814)) << 32);
                 }
             }
+            const int8_t *aq = P.aq;
+            const float *parts = P.in_parts;
+            if (aq != st_q || parts != st_parts || g.s_begin != st_begin || g.cs != st_cs) {
+                const unsigned *wt = P.wait;
+                if (wt && !wait_ready(wt, P.wait_target, status)) {
+                    if (lane == 0) sh.abort = 1u;
+                } else {
+                    if (tr && lane == 0) tr[1] = now();
+                    stage<M>(P, g, act, sh);
+                    if (tr && lane == 0) tr[2] = now();
+                    st_q = aq;
+                    st_parts = parts;
+                    st_begin = g.s_begin;
+                    st_cs = g.cs;
+                }
+            }
+            lds_barrier();   // B1
+            if (sh.abort) break;
         }
-        if (best[threadIdx.x]) max_dev(P.argmax + threadIdx.x, best[threadIdx.x]);
-        best[threadIdx.x] = 0ull;
+        lds_barrier();       // B2: the compute waves have written the unit's partial sums
+        if (sh.abort) break;
+        if (tr && lane == 0 && n_units == 0) tr[3] = now();
+        n_units++;
+        pp = c.p;
+        pu = c.u;
+        pchunk = g.chunk;
+        buf ^= 1;
+        unit_next(tab, n_phases, b, G, c);
     }
-    __syncthreads();
+    if (pp >= 0 && !sh.abort) {
+        ctrl_finish<M>(tab[pp], pu, wpart_buf<M>(smem, buf ^ 1), sh);
+        if (tr && lane == 0) {
+            if (n_units == 1) tr[4] = now();
+            tr[5] = now();
+            tr[6] = n_units;
+        }
+        flush_best<M>(tab[pp].argmax, sh, cleared, status);
+    }
+    drain();
 }
 
-// LDS layout of a workgroup: act chunk [MG][CS * kActRec] | ystage
-// [3][M][kRows] fp32 | wave partials [4][2][M][kRows] fp32 | the input's
-// sums of squares [M][n_parts] fp32.
-template <int M>
-__device__ __forceinline__ void lds_parts(uint8_t *smem, int CS, float *&ystage, float *&wpart, float *&parts) {
-    ystage = reinterpret_cast<float *>(smem + MG<M>::value * CS * kActRec);
-    wpart = ystage + 3 * M * kRows;
-    parts = wpart + 8 * M * kRows;
-}
-
+// ============================================================ kernels
 // One workgroup per unit of a single phase.
 template <int M>
-__global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void phase_kernel(PhaseDesc P, int CS) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void phase_kernel(PhaseDesc P) {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ Shared<M> sh;
-    float *ystage, *wpart, *parts;
-    lds_parts<M>(smem, CS, ystage, wpart, parts);
     if (threadIdx.x < SV_MAX_M) sh.best[threadIdx.x] = 0ull;
-    dispatch_phase<M>(P, blockIdx.x, gridDim.x, static_cast<uint32_t>(P.n_units), smem, ystage, wpart, parts, CS, sh,
-                      nullptr, nullptr);
-    flush_best(P, sh.best, M, nullptr, nullptr);
+    if (threadIdx.x == 0) sh.abort = 0u;
+    __syncthreads();
+    const OneTab tab{P};
+    if (threadIdx.x < kCompWaves * 64) compute_waves<M>(tab, 1, blockIdx.x, gridDim.x, smem, sh);
+    else control_wave<M>(tab, 1, blockIdx.x, gridDim.x, smem, sh, nullptr, nullptr, nullptr);
 }
 
 // ctl: control words (kCtl*), then per phase kPhaseCounters counters of
 // finished units, kSlotStride words apart.  The last workgroup to exit
 // adds the run's status to kCtlResult (an OR the host reads and clears) and
-// returns every other word to zero (and, after an expired wait, the tile counters of split tiles), so
-// the next run starts clean without a reset launch.
+// returns every other word to zero (and, after an expired wait, the tile
+// counters of split tiles), so the next run starts clean without a reset
+// launch.
 template <int M>
-__global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const PhaseDesc *__restrict__ table, int n_phases,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void pass_kernel(const PhaseDesc *__restrict__ table, int n_phases,
                                                         unsigned *ctl, int CS, ArgmaxList am,
                                                         unsigned long long *trace) {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ Shared<M> sh;
-    __shared__ PhaseDesc P;
-    float *ystage, *wpart, *parts;
-    lds_parts<M>(smem, CS, ystage, wpart, parts);
+    __shared__ int last;
     unsigned *status = ctl + kCtlStatus;
     const unsigned *cleared = ctl + kCtlArgmaxClear;
     if (threadIdx.x < SV_MAX_M) sh.best[threadIdx.x] = 0ull;
+    if (threadIdx.x == 0) sh.abort = 0u;
     // Workgroup 0 clears every argmax of the pass, waits until the stores
     // are done and raises the flag flush_best waits on.
     if (blockIdx.x == 0 && am.n > 0) {
@@ -902,35 +1211,14 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const Ph
         __syncthreads();
         if (threadIdx.x == 0) st_dev(ctl + kCtlArgmaxClear, 1u);
     }
-    const uint32_t G = gridDim.x, b = blockIdx.x;
-    int cur = -1;
-    bool ok = true;
-    for (int p = 0; p < n_phases && ok; p++) {
-        // units of phase p are dealt round-robin, continuing where phase
-        // p-1 stopped, so every workgroup gets its share of every phase
-        const uint32_t base = table[p].unit_base, nu = static_cast<uint32_t>(table[p].n_units);
-        uint32_t u = (b + G - base % G) % G;
-        if (u >= nu) continue;
-        if (cur >= 0) flush_best(P, sh.best, M, cleared, status);
-        if (threadIdx.x == 0) P = table[p];
-        __syncthreads();
-        cur = p;
-        unsigned long long *tr = trace ? trace + (static_cast<size_t>(b) * n_phases + p) * kTraceWords : nullptr;
-        if (tr && threadIdx.x == 0) {
-            tr[0] = __builtin_amdgcn_s_memrealtime();
-            // where the workgroup runs: HW_ID (CU, shader array and engine
-            // fields) and XCC_ID, full 32-bit reads of the two registers
-            tr[9] = static_cast<unsigned long long>(__builtin_amdgcn_s_getreg(0xF804)) |
-                    (static_cast<unsigned long long>(__builtin_amdgcn_s_getreg(0xF814)) << 32);
-        }
-        ok = dispatch_phase<M>(P, u, G, nu, smem, ystage, wpart, parts, CS, sh, status, tr);
-    }
-    if (cur >= 0) flush_best(P, sh.best, M, cleared, status);
-    drain();
     __syncthreads();
-    if (threadIdx.x == 0) sh.last = (add_dev(ctl + kCtlExited, 1u) == gridDim.x - 1) ? 1 : 0;
+    const ManyTab tab{reinterpret_cast<const SV_AS4 PhaseDesc *>(reinterpret_cast<uintptr_t>(table))};
+    if (threadIdx.x < kCompWaves * 64) compute_waves<M>(tab, n_phases, blockIdx.x, gridDim.x, smem, sh);
+    else control_wave<M>(tab, n_phases, blockIdx.x, gridDim.x, smem, sh, status, cleared, trace);
     __syncthreads();
-    if (sh.last) {
+    if (threadIdx.x == 0) last = (add_dev(ctl + kCtlExited, 1u) == gridDim.x - 1) ? 1 : 0;
+    __syncthreads();
+    if (last) {
         const unsigned st = ld_dev(status);
         for (int i = 1 + static_cast<int>(threadIdx.x); i < 1 + n_phases * kPhaseCounters; i += kThreads)
             st_dev(ctl + i * kSlotStride, 0u);
@@ -950,4 +1238,5 @@ __global__ __launch_bounds__(kThreads, M <= 8 ? 2 : 1) void pass_kernel(const Ph
         }
     }
 }
+
 }  // namespace sv

@@ -20,7 +20,7 @@ void launch_pass_m<SV_INST_M>(int grid, size_t lds, hipStream_t st, const PhaseD
 
 template <>
 void launch_phase_m<SV_INST_M>(int grid, size_t lds, hipStream_t st, const PhaseDesc &P, int CS) {
-    hipLaunchKernelGGL((phase_kernel<SV_INST_M>), dim3(grid), dim3(kThreads), lds, st, P, CS);
+    hipLaunchKernelGGL((phase_kernel<SV_INST_M>), dim3(grid), dim3(kThreads), lds, st, P);
 }
 
 template <>
@@ -40,6 +40,11 @@ hipError_t allow_lds_m<SV_INST_M>(size_t lds) {
     if (e != hipSuccess) return e;
     return hipFuncSetAttribute(reinterpret_cast<const void *>(&phase_kernel<SV_INST_M>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+}
+
+template <>
+hipError_t pass_attr_m<SV_INST_M>(hipFuncAttributes *fa) {
+    return hipFuncGetAttributes(fa, reinterpret_cast<const void *>(&pass_kernel<SV_INST_M>));
 }
 
 }  // namespace sv

@@ -8,10 +8,10 @@
 
 namespace sv {
 
-constexpr int kThreads = 256;          // four waves
+constexpr int kThreads = 576;          // eight compute waves and one control wave
 constexpr int kRows = 32;              // rows per tile: 2 half tiles of 8 groups x 2 rows
-constexpr int kActRec = 32 + 4 + 8;    // LDS bytes per position per staged sub-block
-constexpr int kMaxChunkSteps = 12;     // most 256-element steps of K one unit covers
+constexpr int kActRec = 32 + 4 + 8;    // LDS bytes per position per staged sub-block (codes, scale, sums)
+constexpr int kMaxChunkSteps = 20;     // most 256-element steps of K one unit covers
 constexpr int kMaxS = 8;               // most K chunks (K <= 24576)
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kMaxGrid = 1024;         // most workgroups a pass launches
@@ -51,7 +51,7 @@ struct PhaseDesc {
     int32_t N, K, wrows;
     int32_t S, steps, n_tiles, per_tile, n_units, chunk_sub;
     int32_t count_all;        // 0: only units of matrix ep_src feed a reader
-    int32_t fused;            // 1: a unit covers both matrices of a Q4_K gate/up pair
+    int32_t fused;            // reserved (0): the matrices of a pair are units of their own
     uint64_t o1, o2, o3;
     const int32_t *row_ids;
     const int8_t *aq;
@@ -93,5 +93,7 @@ template <int M>
 int occupancy_pass_m(size_t lds);
 template <int M>
 hipError_t allow_lds_m(size_t lds);
+template <int M>
+hipError_t pass_attr_m(hipFuncAttributes *fa);
 
 }  // namespace sv

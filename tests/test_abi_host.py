@@ -128,9 +128,9 @@ def test_head_and_accept_rejects():
          sv.SV_ERR_ARG)
     _err(L.sv_head_logits(ctypes.byref(H), ctypes.byref(_act()), FAKE, 0, FAKE, None, None, 0, None),
          sv.SV_ERR_SHAPE)
-    # a split head needs a workspace
-    H2 = _w(qt=14, rows=4096, cols=5120)
-    A2 = _act(K=5120)
+    # a head whose K is split over units (K > 5120) needs a workspace
+    H2 = _w(qt=14, rows=4096, cols=10240)
+    A2 = _act(K=10240)
     need = L.sv_head_workspace_bytes(ctypes.byref(H2), ctypes.byref(A2), 0)
     assert need > 0
     _err(L.sv_head_logits(ctypes.byref(H2), ctypes.byref(A2), None, 0, FAKE, None, None, 0, None),
@@ -150,19 +150,19 @@ def test_head_and_accept_rejects():
 
 
 def test_workspace_sizes():
-    """K is cut into ceil(steps / 12) chunks of 256-element steps; partial sums
+    """K is cut into ceil(steps / 20) chunks of 256-element steps; partial sums
     (after a fixed 256 KiB counter region) are needed when K is split, or
-    when two matrices may be paired and a unit cannot hold both (anything but
-    Q4_K at M <= 8), and nothing otherwise."""
+    when two matrices may be paired (each matrix of a pair is a unit of its
+    own and the tile's last unit forms the product), and nothing otherwise."""
     L = sv.lib()
-    for rows, cols, qt, n_w, M, S in [(2560, 2560, 12, 3, 5, 1), (2560, 9728, 14, 1, 5, 4), (9728, 2560, 12, 2, 16, 1),
-                                      (5120, 17408, 14, 1, 5, 6), (17408, 5120, 12, 1, 8, 2),
-                                      (2560, 2560, 14, 2, 5, 1), (17408, 5120, 12, 2, 5, 2)]:
+    for rows, cols, qt, n_w, M, S in [(2560, 2560, 12, 3, 5, 1), (2560, 9728, 14, 1, 5, 2), (9728, 2560, 12, 2, 16, 1),
+                                      (5120, 17408, 14, 1, 5, 4), (17408, 5120, 12, 1, 8, 1),
+                                      (2560, 2560, 14, 2, 5, 1), (17408, 5120, 12, 2, 5, 1), (4096, 10240, 14, 1, 3, 2)]:
         steps = -(-cols // 256)
-        assert -(-steps // 12) == S
+        assert -(-steps // 20) == S
         W = (sv.Weight * n_w)(*([_w(qt=qt, rows=rows, cols=cols)] * n_w))
         need = L.sv_matvec_workspace_bytes(W, n_w, ctypes.byref(_act(M=M, K=cols)))
-        if S == 1 and (n_w != 2 or (qt == 12 and M <= 8)):
+        if S == 1 and n_w != 2:
             assert need == 0
         else:
             assert need == 256 * 1024 + n_w * S * M * rows * 4
