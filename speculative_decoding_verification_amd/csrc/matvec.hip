@@ -109,9 +109,10 @@ static void decompose(PhaseDesc &P) {
     P.steps = static_cast<int>((nsub + 7) / 8);
     P.S = std::max(1, (P.steps + kMaxChunkSteps - 1) / kMaxChunkSteps);
     P.n_tiles = static_cast<int>((static_cast<int64_t>(P.N) + kRows - 1) / kRows);
-    // The matrices of a gate/up pair are units of their own; the tile's
-    // last unit forms the product.
-    P.fused = 0;
+    // For M <= 8 a unit of a gate/up pair covers both matrices; above that
+    // each matrix is a unit of its own and the tile's last unit forms the
+    // product.
+    P.fused = (P.ep_mode == SV_EP_PAIR && P.n_w == 2 && P.M <= 8) ? 1 : 0;
     P.per_tile = P.S * (P.fused ? 1 : P.n_w);
     P.n_units = P.n_tiles * P.per_tile;
     P.chunk_sub = ((P.steps + P.S - 1) / P.S) * 8;
@@ -120,7 +121,7 @@ static void decompose(PhaseDesc &P) {
 // LDS of a workgroup: the compute waves' partial sums (two buffers), then
 // the staged input chunk of all M positions and, for an RMS-normalised
 // input, its partials; the largest phase sets the size.
-static size_t wpart_bytes(int M) { return static_cast<size_t>(2) * 8 * M * 16 * 4; }
+static size_t wpart_bytes(int M) { return static_cast<size_t>(2) * 8 * 2 * M * 16 * 4; }
 
 static size_t phase_lds(const PhaseDesc &P, int M) {
     return static_cast<size_t>(M) * P.chunk_sub * kActRec + (P.in_parts ? static_cast<size_t>(M) * P.n_parts * 4 : 0);

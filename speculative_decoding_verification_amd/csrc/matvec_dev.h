@@ -10,9 +10,10 @@
 // a cycle separated by synchronisation between phases).
 //
 // Work decomposition.  A phase (one to three matrices sharing an input) is
-// cut into units = (32-row tile, K chunk, matrix); the two matrices of a
-// gate/up pair are units of their own whose values meet in the control
-// wave of the tile's last unit.  K is walked in steps of 256 elements (one K-quant super-block,
+// cut into units = (32-row tile, K chunk, matrix); for M <= 8 a unit of a
+// gate/up pair covers both matrices (their items alternate in the ring and
+// the product forms in the control wave), above that each matrix is a unit
+// of its own and the values meet in the tile's last unit.  K is walked in steps of 256 elements (one K-quant super-block,
 // eight Q8_0 blocks); a chunk is at most 20 steps (5120 elements), so
 // S(K) = ceil(steps / 20) depends on K alone.
 //
@@ -140,7 +141,8 @@ __device__ __forceinline__ WaveSpan wave_span(const PD &P, const UnitPos &g, int
     s.w0 = g.c0 + part * tc / kStepParts;
     s.w1 = g.c0 + (part + 1) * tc / kStepParts;
     s.sp = P.qtype == SV_Q4_K ? 2 : 1;
-    s.nitems = max(1, (s.w1 - s.w0 + s.sp - 1) / s.sp);
+    // a fused pair alternates gate and up items over the same steps
+    s.nitems = max(1, (s.w1 - s.w0 + s.sp - 1) / s.sp) * (P.fused ? 2 : 1);
     return s;
 }
 
@@ -452,15 +454,15 @@ struct Shared {
     unsigned abort;
 };
 
-// Dynamic LDS: wave partials [2 buffers][8 waves][M][16 rows] fp32, then
-// the staged input chunk and its RMS partials.
+// Dynamic LDS: wave partials [2 buffers][8 waves][2 matrices][M][16 rows]
+// fp32, then the staged input chunk and its RMS partials.
 template <int M>
 __device__ __forceinline__ float *wpart_buf(uint8_t *smem, int buf) {
-    return reinterpret_cast<float *>(smem) + buf * (kCompWaves * M * 16);
+    return reinterpret_cast<float *>(smem) + buf * (kCompWaves * 2 * M * 16);
 }
 template <int M>
 __device__ __forceinline__ uint8_t *act_base(uint8_t *smem) {
-    return smem + 2 * kCompWaves * M * 16 * 4;
+    return smem + 2 * kCompWaves * 2 * M * 16 * 4;
 }
 
 // Trace record of a (workgroup, phase) (control wave): real-time counter at
@@ -478,7 +480,7 @@ struct ItemCur {
     // phase
     const uint8_t *w0, *w1, *w2;
     const uint8_t *wm;   // matrix of the current unit
-    int qtype, K, N, wrows;
+    int qtype, fused, K, N, wrows;
     uint64_t o1, o2, o3;
     const int32_t *row_ids;
     // unit
@@ -495,6 +497,7 @@ __device__ __forceinline__ void cur_phase(const Tab &tab, ItemCur &c) {
     c.w1 = P.w[1];
     c.w2 = P.w[2];
     c.qtype = P.qtype;
+    c.fused = P.fused;
     c.K = P.K;
     c.N = P.N;
     c.wrows = P.wrows;
@@ -612,14 +615,19 @@ __device__ __forceinline__ void load_item(Slot &s, const ItemCur &c) {
     const int64_t r0 = c.srow[0], r1 = c.srow[1];
     const int64_t K = c.K, nsub = K >> 5, nsb = K >> 8;
     const bool q4 = c.qtype == SV_Q4_K;
-    const int t = c.s.w0 + c.item * (q4 ? 2 : 1);
+    // a fused pair's item 2k is gate, 2k + 1 up, over the same steps
+    const int it = c.fused ? (c.item >> 1) : c.item;
+    const uint64_t odd = c.fused ? static_cast<uint64_t>(c.item & 1) : 0u;
+    const uint8_t *wsel = reinterpret_cast<const uint8_t *>((1u - odd) * reinterpret_cast<uint64_t>(c.wm) +
+                                                            odd * reinterpret_cast<uint64_t>(c.w1));
+    const int t = c.s.w0 + it * (q4 ? 2 : 1);
     const int64_t fb = c.g.s_begin + (c.qtype == SV_Q8_0 ? 0 : jl);
     const int64_t sa = item_sb(c, t, fb);
     const int64_t sb = q4 ? item_sb(c, t + 1, fb) : sa;
     const uint8_t *a0, *a1, *a2, *a3, *b0, *b1, *b2, *b3, *b4, *b5, *b6, *b7;
     if (q4) {
         // records: (r0, sa), (r1, sa), (r0, sb), (r1, sb)
-        const uint8_t *w = c.wm;
+        const uint8_t *w = wsel;
         a0 = w + (r0 * nsub + sa) * 16;
         a1 = w + (r1 * nsub + sa) * 16;
         a2 = w + (r0 * nsub + sb) * 16;
@@ -634,27 +642,27 @@ __device__ __forceinline__ void load_item(Slot &s, const ItemCur &c) {
         b5 = b4 + 2;
         b7 = b6 + 2;
     } else if (c.qtype == SV_Q6_K) {
-        a0 = c.wm + (r0 * nsub + sa) * 16;
-        a1 = c.wm + (r1 * nsub + sa) * 16;
+        a0 = wsel + (r0 * nsub + sa) * 16;
+        a1 = wsel + (r1 * nsub + sa) * 16;
         // 16 bytes from the 8-byte high-bit record: the stream is followed by
         // the scale streams, so the extra 8 bytes stay inside the matrix
-        a2 = c.wm + c.o1 + (r0 * nsub + sa) * 8;
-        a3 = c.wm + c.o1 + (r1 * nsub + sa) * 8;
-        b0 = c.wm + c.o2 + r0 * (K >> 4) + 2 * sa;
-        b1 = c.wm + c.o2 + r1 * (K >> 4) + 2 * sa;
-        b2 = c.wm + c.o3 + (r0 * nsb + (sa >> 3)) * 2;
-        b3 = c.wm + c.o3 + (r1 * nsb + (sa >> 3)) * 2;
+        a2 = wsel + c.o1 + (r0 * nsub + sa) * 8;
+        a3 = wsel + c.o1 + (r1 * nsub + sa) * 8;
+        b0 = wsel + c.o2 + r0 * (K >> 4) + 2 * sa;
+        b1 = wsel + c.o2 + r1 * (K >> 4) + 2 * sa;
+        b2 = wsel + c.o3 + (r0 * nsb + (sa >> 3)) * 2;
+        b3 = wsel + c.o3 + (r1 * nsb + (sa >> 3)) * 2;
         b4 = b0;
         b5 = b1;
         b6 = b2;
         b7 = b3;
     } else {
-        a0 = c.wm + r0 * K + sa * 32;
+        a0 = wsel + r0 * K + sa * 32;
         a1 = a0 + 16;
-        a2 = c.wm + r1 * K + sa * 32;
+        a2 = wsel + r1 * K + sa * 32;
         a3 = a2 + 16;
-        b0 = c.wm + c.o1 + (r0 * nsub + sa) * 2;
-        b1 = c.wm + c.o1 + (r1 * nsub + sa) * 2;
+        b0 = wsel + c.o1 + (r0 * nsub + sa) * 2;
+        b1 = wsel + c.o1 + (r1 * nsub + sa) * 2;
         b2 = b0;
         b3 = b1;
         b4 = b0;
@@ -699,12 +707,13 @@ template <int M>
 __device__ __forceinline__ void consume(const Slot &s, const ItemCur &c, const ActLds &A, float (&acc)[2][M]) {
     const int jl = threadIdx.x & 7;
     const int64_t nsub = c.K >> 5;
+    const int it = c.fused ? (c.item >> 1) : c.item;
     if (c.qtype == SV_Q4_K) {
-        const int t = c.s.w0 + c.item * 2;
+        const int t = c.s.w0 + it * 2;
         if (t < c.s.w1) step_terms<SV_Q4_K, 0, M>(s, A, t * 8 + jl - c.g.s_begin, acc);
         if (t + 1 < c.s.w1) step_terms<SV_Q4_K, 2, M>(s, A, (t + 1) * 8 + jl - c.g.s_begin, acc);
     } else {
-        const int t = c.s.w0 + c.item;
+        const int t = c.s.w0 + it;
         const int64_t sb = static_cast<int64_t>(t) * 8 + jl;
         if (t < c.s.w1 && sb < nsub) {
             const int sl = static_cast<int>(sb) - c.g.s_begin;
@@ -715,9 +724,10 @@ __device__ __forceinline__ void consume(const Slot &s, const ItemCur &c, const A
 }
 
 // End of a unit: the fixed-order sum of each row group's 8 lanes, written
-// to the wave's partial slots [wave][position][row of the half tile].
+// to the wave's partial slots [wave][matrix][position][row of the half
+// tile] (matrix 1: the up half of a fused pair).
 template <int M>
-__device__ __forceinline__ void put_partials(float *wp, float (&acc)[2][M]) {
+__device__ __forceinline__ void put_partials(float *wp, float (&acc)[2][M], int mm) {
     const int lane = threadIdx.x & 63;
     const int wave = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
     const int grp = lane >> 3, jl = lane & 7;
@@ -726,7 +736,7 @@ __device__ __forceinline__ void put_partials(float *wp, float (&acc)[2][M]) {
 #pragma unroll
         for (int m = 0; m < M; m++) {
             const float v = group8_sum(acc[p][m]);
-            if (jl == 0) wp[(wave * M + m) * 16 + grp * 2 + p] = v;
+            if (jl == 0) wp[((wave * 2 + mm) * M + m) * 16 + grp * 2 + p] = v;
             acc[p][m] = 0.0f;
         }
 }
@@ -738,7 +748,8 @@ struct CompState {
     bool lv, go;      // load cursor not yet past the end; compute cursor valid and no abort
     int buf;          // wave-partial buffer of the current unit
     ActLds A;
-    float acc[2][M];
+    float acc[2][M];              // matrix of the unit (gate of a fused pair)
+    float accu[M <= 8 ? 2 : 1][M]; // up of a fused pair (M <= 8 only)
 };
 
 // One ring step: consume the item in slot s (if the compute cursor is
@@ -754,11 +765,20 @@ __device__ __forceinline__ void ring_step(const Tab &tab, int n_phases, uint32_t
         if (sh.abort) st.go = false;
         else st.A = act_lds(act_base<M>(smem), M, st.C.g.cs);
     }
-    if (st.go) consume<M>(s, st.C, st.A, st.acc);
+    if (st.go) {
+        if constexpr (M <= 8) {
+            if (st.C.fused && (st.C.item & 1)) consume<M>(s, st.C, st.A, st.accu);
+            else consume<M>(s, st.C, st.A, st.acc);
+        } else {
+            consume<M>(s, st.C, st.A, st.acc);
+        }
+    }
     load_item(s, st.L);
     if (st.lv) st.lv = cur_advance_keep(tab, n_phases, b, G, st.L, wave, true);
     if (st.go && st.C.item == st.C.s.nitems - 1) {
-        put_partials<M>(wpart_buf<M>(smem, st.buf), st.acc);
+        put_partials<M>(wpart_buf<M>(smem, st.buf), st.acc, 0);
+        if constexpr (M <= 8)
+            if (st.C.fused) put_partials<M>(wpart_buf<M>(smem, st.buf), st.accu, 1);
         lds_barrier();   // B2: the unit's partial sums are written
         st.buf ^= 1;
         if (sh.abort) st.go = false;
@@ -787,6 +807,10 @@ __device__ __forceinline__ void compute_waves(const Tab &tab, int n_phases, uint
     for (int p = 0; p < 2; p++)
 #pragma unroll
         for (int m = 0; m < M; m++) st.acc[p][m] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < (M <= 8 ? 2 : 1); p++)
+#pragma unroll
+        for (int m = 0; m < M; m++) st.accu[p][m] = 0.0f;
     // separate slots (no array): every access has a constant address from
     // the start, so the slots live in registers
     Slot s0, s1, s2, s3;
@@ -830,6 +854,31 @@ __device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target,
     }
 }
 
+// Copies n bytes (a multiple of 4) from global memory to LDS with the
+// loads' LDS transfer: 16 bytes per lane when the source and the size allow
+// it, else 4.  Lane l of an instruction writes dst + 16 l (or 4 l), so the
+// LDS destination of each instruction is uniform.
+__device__ __forceinline__ void dma_copy(uint8_t *dst, const uint8_t *src, int n) {
+    const int lane = threadIdx.x & 63;
+    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | static_cast<uintptr_t>(n)) & 15) == 0) {
+        const int n16 = n >> 4;
+        for (int k = 0; 64 * k < n16; k++) {
+            const int i = 64 * k + lane;
+            if (i < n16)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + i * 16),
+                                                 (SV_AS3 void *)(dst + 64 * k * 16), 16, 0, 0);
+        }
+    } else {
+        const int n4 = n >> 2;
+        for (int k = 0; 64 * k < n4; k++) {
+            const int i = 64 * k + lane;
+            if (i < n4)
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + i * 4),
+                                                 (SV_AS3 void *)(dst + 64 * k * 4), 4, 0, 0);
+        }
+    }
+}
+
 // Copies the input chunk of a phase (codes, scales, code sums and, if the
 // input is RMS-normalised, its partials) into LDS with load-to-LDS
 // transfers, then forms the RMS factors: lane l adds partials l, l + 64,
@@ -850,39 +899,15 @@ __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *ac
     float *pd = reinterpret_cast<float *>(act + M * cs * 44);
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(aq) + static_cast<int64_t>(m) * K +
-                             static_cast<int64_t>(g.s_begin) * 32;
-        const int n16 = cs * 2;
-        for (int k = 0; 64 * k < n16; k++) {
-            const int i = 64 * k + lane;
-            if (i < n16)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + i * 16),
-                                                 (SV_AS3 void *)(qd + m * cs * 32 + 64 * k * 16), 16, 0, 0);
-        }
-        const float *dsrc = ad + static_cast<int64_t>(m) * nsub + g.s_begin;
-        for (int k = 0; 64 * k < cs; k++) {
-            const int i = 64 * k + lane;
-            if (i < cs)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(dsrc + i),
-                                                 (SV_AS3 void *)(dd + m * cs + 64 * k), 4, 0, 0);
-        }
-        const int32_t *xsrc = as16 + static_cast<int64_t>(m) * (K >> 4) + 2 * g.s_begin;
-        for (int k = 0; 64 * k < 2 * cs; k++) {
-            const int i = 64 * k + lane;
-            if (i < 2 * cs)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(xsrc + i),
-                                                 (SV_AS3 void *)(xd + m * 2 * cs + 64 * k), 4, 0, 0);
-        }
+        dma_copy(qd + m * cs * 32,
+                 reinterpret_cast<const uint8_t *>(aq) + static_cast<int64_t>(m) * K + static_cast<int64_t>(g.s_begin) * 32,
+                 cs * 32);
+        dma_copy(reinterpret_cast<uint8_t *>(dd + m * cs),
+                 reinterpret_cast<const uint8_t *>(ad + static_cast<int64_t>(m) * nsub + g.s_begin), cs * 4);
+        dma_copy(reinterpret_cast<uint8_t *>(xd + m * 2 * cs),
+                 reinterpret_cast<const uint8_t *>(as16 + static_cast<int64_t>(m) * (K >> 4) + 2 * g.s_begin), cs * 8);
     }
-    if (parts) {
-        const int total = M * n_parts;
-        for (int k = 0; 64 * k < total; k++) {
-            const int f = 64 * k + lane;
-            if (f < total)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(parts + f),
-                                                 (SV_AS3 void *)(pd + 64 * k), 4, 0, 0);
-        }
-    }
+    if (parts) dma_copy(reinterpret_cast<uint8_t *>(pd), reinterpret_cast<const uint8_t *>(parts), M * n_parts * 4);
     // the transfers have written LDS once this wave's loads are complete
     __builtin_amdgcn_s_waitcnt(0);
     for (int m = 0; m < M; m++) {
@@ -951,7 +976,7 @@ __device__ __forceinline__ void store_y(const PD &P, int mt, int64_t row0, const
 // 32-row block, i.e. of one activation block.
 template <int M, class PD>
 __device__ __forceinline__ void finish_tile(const PD &P, int64_t row0, const TileVals<M> &x, const TileVals<M> &e,
-                                            bool do_ep, Shared<M> &sh) {
+                                            bool do_ep, float g_row, Shared<M> &sh) {
     const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
     const int64_t N = P.N;
     const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), N - row0));
@@ -968,7 +993,6 @@ __device__ __forceinline__ void finish_tile(const PD &P, int64_t row0, const Til
     }
     if (do_ep && P.ep_mode != SV_EP_NONE && rows_here == kRows) {
         const float *gamma = P.gamma;
-        const float g_row = gamma ? gld(gamma + row0 + r) : 1.0f;
         int8_t *oq = P.oq;
         float *od = P.od, *osumsq = P.osumsq;
         int32_t *os16 = P.os16;
@@ -998,43 +1022,77 @@ __device__ __forceinline__ void finish_tile(const PD &P, int64_t row0, const Til
     }
 }
 
+// The norm weight of the epilogue for row lane & 31 of unit u's tile,
+// requested before the unit's barrier so it has arrived when the epilogue
+// runs (1 when there is none).
+template <class PD>
+__device__ __forceinline__ float gamma_of(const PD &P, uint32_t u) {
+    const float *gamma = P.gamma;
+    if (!gamma || P.ep_mode == SV_EP_NONE) return 1.0f;
+    const int64_t row = static_cast<int64_t>(static_cast<int>(u) / P.per_tile) * kRows + (threadIdx.x & 31);
+    return row < P.N ? gld(gamma + row) : 1.0f;
+}
+
 // The control wave's part of a unit whose partial sums sit in wave-partial
-// buffer wp: adds the four step quarters of each row in order, then either
-// finishes the tile, or (K split over units, or one matrix of a gate/up
-// pair) stores the chunk's values, and the last unit of the tile to arrive
-// adds all chunks in chunk order (and forms g * u) and finishes it.  Then the unit is
-// handed off if a later phase reads it.
+// buffer wp: adds the four step quarters of each row in order (for both
+// matrices of a fused pair), then either finishes the tile, or (K split over
+// units, or a pair whose matrices sit in two units) stores the chunk's
+// values, and the last unit of the tile to arrive adds all chunks in chunk
+// order and finishes it.  Then the unit is handed off if a later phase
+// reads it.
 template <int M, class PD>
-__device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float *wp, Shared<M> &sh) {
+__device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float *wp, float g_row, Shared<M> &sh) {
     const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5, hr = r >> 4, rr = r & 15;
     const UnitPos g = unit_pos(P, u);
     const int64_t row0 = static_cast<int64_t>(g.tile) * kRows;
     const int64_t N = P.N;
+    const int nm = P.fused ? 2 : 1;
     const bool pair = P.ep_mode == SV_EP_PAIR;
-    const bool split = P.S > 1 || pair;
+    const bool split = P.S > 1 || (pair && !P.fused);
     // the step quarters of each row, added in order: waves hr, hr + 2, ...
-    TileVals<M> v0;
+    TileVals<M> v0, v1;
 #pragma unroll
     for (int k = 0; k < (M + 1) / 2; k++) {
         const int m = min(h + 2 * k, M - 1);
-        float v = wp[(hr * M + m) * 16 + rr];
+        float a = wp[((hr * 2 + 0) * M + m) * 16 + rr];
+        float c = wp[((hr * 2 + 1) * M + m) * 16 + rr];
 #pragma unroll
-        for (int q = 1; q < kStepParts; q++) v += wp[((hr + 2 * q) * M + m) * 16 + rr];
-        v0.v[k] = v;
+        for (int q = 1; q < kStepParts; q++) {
+            a += wp[(((hr + 2 * q) * 2 + 0) * M + m) * 16 + rr];
+            c += wp[(((hr + 2 * q) * 2 + 1) * M + m) * 16 + rr];
+        }
+        v0.v[k] = a;
+        v1.v[k] = c;
     }
     if (!split) {
 #pragma unroll
-        for (int k = 0; k < (M + 1) / 2; k++) v0.v[k] *= sh.rscale[min(h + 2 * k, M - 1)];
+        for (int k = 0; k < (M + 1) / 2; k++) {
+            const float rs = sh.rscale[min(h + 2 * k, M - 1)];
+            v0.v[k] *= rs;
+            v1.v[k] *= rs;
+        }
         store_y<M>(P, g.mat, row0, v0);
-        finish_tile<M>(P, row0, v0, v0, g.mat == P.ep_src, sh);
+        TileVals<M> e = v0;
+        if (nm == 2) {
+            store_y<M>(P, g.mat + 1, row0, v1);
+#pragma unroll
+            for (int k = 0; k < (M + 1) / 2; k++) e.v[k] = v0.v[k] * v1.v[k];
+        }
+        finish_tile<M>(P, row0, v0, e, nm == 2 || g.mat == P.ep_src, g_row, sh);
     } else {
         float *partial = P.partial;
         const int S = P.S;
 #pragma unroll
-        for (int k = 0; k < (M + 1) / 2; k++) {
-            const int m = h + 2 * k;
-            if (m < M && row0 + r < N)
-                st_dev(partial + ((static_cast<int64_t>(g.mat) * S + g.chunk) * M + m) * N + row0 + r, v0.v[k]);
+        for (int mm = 0; mm < 2; mm++) {
+            if (mm < nm) {
+#pragma unroll
+                for (int k = 0; k < (M + 1) / 2; k++) {
+                    const int m = h + 2 * k;
+                    if (m < M && row0 + r < N)
+                        st_dev(partial + ((static_cast<int64_t>(g.mat + mm) * S + g.chunk) * M + m) * N + row0 + r,
+                               mm ? v1.v[k] : v0.v[k]);
+                }
+            }
         }
         drain();
         unsigned *tc = P.tile_count;
@@ -1080,7 +1138,7 @@ __device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float
                 }
             }
             if (lane == 0) st_dev(tc + g.tile, 0u);
-            finish_tile<M>(P, row0, f0, e, true, sh);
+            finish_tile<M>(P, row0, f0, e, true, g_row, sh);
         }
     }
     // hand-off: only units a later phase reads are counted
@@ -1106,12 +1164,13 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
     int st_begin = -1, st_cs = -1;
     unsigned long long *tr = nullptr;
     unsigned n_units = 0;
+    float g_prev = 1.0f;    // norm weight of the previous unit's epilogue row
     uint8_t *act = act_base<M>(smem);
     while (c.p < n_phases) {
         const auto &P = tab[c.p];
         const UnitPos g = unit_pos(P, c.u);
         if (pp >= 0) {
-            ctrl_finish<M>(tab[pp], pu, wpart_buf<M>(smem, buf ^ 1), sh);
+            ctrl_finish<M>(tab[pp], pu, wpart_buf<M>(smem, buf ^ 1), g_prev, sh);
             if (tr && lane == 0) {
                 if (n_units == 1) tr[4] = now();
                 tr[5] = now();
@@ -1149,6 +1208,7 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
             lds_barrier();   // B1
             if (sh.abort) break;
         }
+        g_prev = gamma_of(P, c.u);   // in flight while the unit computes
         lds_barrier();       // B2: the compute waves have written the unit's partial sums
         if (sh.abort) break;
         if (tr && lane == 0 && n_units == 0) tr[3] = now();
@@ -1160,7 +1220,7 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
         unit_next(tab, n_phases, b, G, c);
     }
     if (pp >= 0 && !sh.abort) {
-        ctrl_finish<M>(tab[pp], pu, wpart_buf<M>(smem, buf ^ 1), sh);
+        ctrl_finish<M>(tab[pp], pu, wpart_buf<M>(smem, buf ^ 1), g_prev, sh);
         if (tr && lane == 0) {
             if (n_units == 1) tr[4] = now();
             tr[5] = now();

@@ -51,7 +51,7 @@ struct PhaseDesc {
     int32_t N, K, wrows;
     int32_t S, steps, n_tiles, per_tile, n_units, chunk_sub;
     int32_t count_all;        // 0: only units of matrix ep_src feed a reader
-    int32_t fused;            // reserved (0): the matrices of a pair are units of their own
+    int32_t fused;            // 1: a unit covers both matrices of a gate/up pair (M <= 8)
     uint64_t o1, o2, o3;
     const int32_t *row_ids;
     const int8_t *aq;

@@ -152,8 +152,9 @@ def test_head_and_accept_rejects():
 def test_workspace_sizes():
     """K is cut into ceil(steps / 20) chunks of 256-element steps; partial sums
     (after a fixed 256 KiB counter region) are needed when K is split, or
-    when two matrices may be paired (each matrix of a pair is a unit of its
-    own and the tile's last unit forms the product), and nothing otherwise."""
+    when two matrices may be paired at M > 8 (then each matrix of a pair is a
+    unit of its own and the tile's last unit forms the product; at M <= 8 a
+    unit covers both), and nothing otherwise."""
     L = sv.lib()
     for rows, cols, qt, n_w, M, S in [(2560, 2560, 12, 3, 5, 1), (2560, 9728, 14, 1, 5, 2), (9728, 2560, 12, 2, 16, 1),
                                       (5120, 17408, 14, 1, 5, 4), (17408, 5120, 12, 1, 8, 1),
@@ -162,7 +163,7 @@ def test_workspace_sizes():
         assert -(-steps // 20) == S
         W = (sv.Weight * n_w)(*([_w(qt=qt, rows=rows, cols=cols)] * n_w))
         need = L.sv_matvec_workspace_bytes(W, n_w, ctypes.byref(_act(M=M, K=cols)))
-        if S == 1 and n_w != 2:
+        if S == 1 and (n_w != 2 or M <= 8):
             assert need == 0
         else:
             assert need == 256 * 1024 + n_w * S * M * rows * 4
