@@ -135,6 +135,16 @@ def repacked_bytes(qtype: int, rows: int, cols: int) -> int:
     return int(lib().sv_repacked_bytes(qtype, rows, cols))
 
 
+_GGUF_BLOCK = {8: (32, 34), 12: (256, 144), 14: (256, 210)}   # elements, bytes per GGUF block
+
+
+def gguf_bytes(qtype: int, rows: int, cols: int) -> int:
+    """Bytes of a rows x cols matrix in its canonical GGUF blocks (the
+    weight bytes a projection has to read)."""
+    n, b = _GGUF_BLOCK[qtype]
+    return rows * (cols // n) * b
+
+
 def repack_weights(qtype, gguf, dst, rows, cols, stream=None):
     _check(lib().sv_repack_weights(qtype, _ptr(gguf), _ptr(dst), rows, cols, _stream(stream)))
 

@@ -32,7 +32,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 from . import (SV_EP_PAIR, SV_EP_QUANT, SV_Q4_K, SV_Q6_K, SV_Q8_0, Pass, accept_greedy, act, epilogue,
-               head_logits, phase, quantize_act_q8, repack_weights, repacked_bytes, verify_matvec, weight)
+               gguf_bytes, head_logits, phase, quantize_act_q8, repack_weights, repacked_bytes, verify_matvec, weight)
 
 
 @dataclass
@@ -54,10 +54,10 @@ class StackShape:
                 ("down", self.down_q, H, F)]
 
     def layer_bytes(self) -> int:
-        return sum(repacked_bytes(qt, r, c) for _, qt, r, c in self.layer_mats())
+        return sum(gguf_bytes(qt, r, c) for _, qt, r, c in self.layer_mats())
 
     def head_bytes(self) -> int:
-        return repacked_bytes(self.head_q, self.vocab, self.hidden) if self.vocab else 0
+        return gguf_bytes(self.head_q, self.vocab, self.hidden) if self.vocab else 0
 
     def pass_bytes(self) -> int:
         return self.layers * self.layer_bytes() + self.head_bytes()
@@ -100,11 +100,11 @@ class LayerWeights:
 def upload_gguf(qtype: int, raw: np.ndarray, rows: int, cols: int, staging=None):
     """Copy canonical GGUF bytes to the GPU and repack them (load time)."""
     t = _torch()
-    n = repacked_bytes(qtype, rows, cols)
-    assert n == raw.size, (n, raw.size)
-    src = t.from_numpy(raw.reshape(-1)).cuda() if staging is None else staging[:n].copy_(
+    g = gguf_bytes(qtype, rows, cols)
+    assert g == raw.size, (g, raw.size)
+    src = t.from_numpy(raw.reshape(-1)).cuda() if staging is None else staging[:g].copy_(
         t.from_numpy(raw.reshape(-1)), non_blocking=False)
-    dst = t.empty(n, dtype=t.uint8, device="cuda")
+    dst = t.empty(repacked_bytes(qtype, rows, cols), dtype=t.uint8, device="cuda")
     assert dst.data_ptr() % 256 == 0
     repack_weights(qtype, src, dst, rows, cols)
     return weight(qtype, rows, cols, dst), dst
@@ -121,7 +121,7 @@ class VerifyStack:
         t = _torch()
         self.shape, self.eps, self.max_M = shape, eps, max_M
         H, F = shape.hidden, shape.ffn
-        staging = t.empty(max(repacked_bytes(qt, r, c) for _, qt, r, c in shape.layer_mats()) + 256,
+        staging = t.empty(max(gguf_bytes(qt, r, c) for _, qt, r, c in shape.layer_mats()) + 256,
                           dtype=t.uint8, device="cuda")
         self.layers = []
         n_workers = workers or max(1, min(16, os.cpu_count() or 1))
@@ -254,17 +254,17 @@ class VerifyStack:
         sh = self.shape
         H, F = sh.hidden, sh.ffn
         if label == "qkv":
-            return 2 * repacked_bytes(sh.attn_q, H, H) + repacked_bytes(sh.v_q, H, H)
+            return 2 * gguf_bytes(sh.attn_q, H, H) + gguf_bytes(sh.v_q, H, H)
         if label == "v":
-            return repacked_bytes(sh.v_q, H, H)
+            return gguf_bytes(sh.v_q, H, H)
         if label == "qk":
-            return 2 * repacked_bytes(sh.attn_q, H, H)
+            return 2 * gguf_bytes(sh.attn_q, H, H)
         if label == "o":
-            return repacked_bytes(sh.attn_q, H, H)
+            return gguf_bytes(sh.attn_q, H, H)
         if label == "gate_up":
-            return 2 * repacked_bytes(sh.gate_up_q, F, H)
+            return 2 * gguf_bytes(sh.gate_up_q, F, H)
         if label == "down":
-            return repacked_bytes(sh.down_q, H, F)
+            return gguf_bytes(sh.down_q, H, F)
         if label == "head":
             return sh.head_bytes()
         return 0

@@ -103,19 +103,52 @@ static int prepare_lds(int M, size_t lds) {
     return hip_check(kLdsFns[M - 1](lds), "allow LDS");
 }
 
-// Decomposition of a phase: a function of K, rows and the matrix count only.
-static void decompose(PhaseDesc &P) {
+// Decomposition of a phase.  K is cut into S = ceil(steps / 20) chunks.
+// A balanced phase (every projection that is not a head) with at least a
+// round of kBalanceGrid tile-chunks also cuts the tiles of its last partial
+// round finer: the remainder R of tile-chunks over whole rounds is spread as
+// S1 = f S chunks on the last ceil(R / S) tiles, so the phase fills whole
+// rounds and no workgroup runs a full unit while the others wait.  The
+// chunking is a function of K and the row count only (not of M, nor of the
+// other matrices of the call), so the batch invariance of every row holds;
+// a head keeps S chunks on every tile, so a restricted head scores a row
+// exactly as the full head does.
+static FastDiv fast_div(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) l++;
+    const unsigned __int128 num = static_cast<unsigned __int128>(1) << (31 + l);
+    return FastDiv{static_cast<uint32_t>((num + d - 1) / d), 31 + l};
+}
+
+static void decompose(PhaseDesc &P, bool balance) {
     const int64_t nsub = P.K / 32;
     P.steps = static_cast<int>((nsub + 7) / 8);
     P.S = std::max(1, (P.steps + kMaxChunkSteps - 1) / kMaxChunkSteps);
     P.n_tiles = static_cast<int>((static_cast<int64_t>(P.N) + kRows - 1) / kRows);
+    P.S1 = P.S;
+    P.T1 = P.n_tiles;
+    const int64_t tc = static_cast<int64_t>(P.n_tiles) * P.S;
+    if (balance && tc >= kBalanceGrid && tc % kBalanceGrid) {
+        const int64_t R = tc % kBalanceGrid;
+        const int tr = static_cast<int>((R + P.S - 1) / P.S);
+        const int f = std::min({kBalanceGrid / (tr * P.S), kMaxS / P.S, P.steps / P.S});
+        if (f >= 2) {
+            P.T1 = P.n_tiles - tr;
+            P.S1 = P.S * f;
+        }
+    }
     // For M <= 8 a unit of a gate/up pair covers both matrices; above that
     // each matrix is a unit of its own and the tile's last unit forms the
     // product.
     P.fused = (P.ep_mode == SV_EP_PAIR && P.n_w == 2 && P.M <= 8) ? 1 : 0;
-    P.per_tile = P.S * (P.fused ? 1 : P.n_w);
-    P.n_units = P.n_tiles * P.per_tile;
+    P.mu = P.fused ? 1 : P.n_w;
+    P.per_tile = P.S * P.mu;
+    P.n_units = P.T1 * P.per_tile + (P.n_tiles - P.T1) * P.S1 * P.mu;
     P.chunk_sub = ((P.steps + P.S - 1) / P.S) * 8;
+    P.div_pt = fast_div(static_cast<uint32_t>(P.per_tile));
+    P.div_S = fast_div(static_cast<uint32_t>(P.S));
+    P.div_f = fast_div(static_cast<uint32_t>(P.S1 / P.S));
+    P.div_S1 = fast_div(static_cast<uint32_t>(P.S1));
 }
 
 // LDS of a workgroup: the compute waves' partial sums (two buffers), then
@@ -127,11 +160,13 @@ static size_t phase_lds(const PhaseDesc &P, int M) {
     return static_cast<size_t>(M) * P.chunk_sub * kActRec + (P.in_parts ? static_cast<size_t>(M) * P.n_parts * 4 : 0);
 }
 
-static bool needs_partials(const PhaseDesc &P) { return P.S > 1 || (P.ep_mode == SV_EP_PAIR && !P.fused); }
+static bool needs_partials(const PhaseDesc &P) {
+    return P.S1 > 1 || (P.ep_mode == SV_EP_PAIR && !P.fused);
+}
 
 static size_t partial_bytes(const PhaseDesc &P, int M) {
     if (!needs_partials(P)) return 0;
-    return static_cast<size_t>(P.n_w) * P.S * M * static_cast<size_t>(P.N) * 4;
+    return static_cast<size_t>(P.n_w) * P.S1 * M * static_cast<size_t>(P.N) * 4;
 }
 
 static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
@@ -141,7 +176,7 @@ static int validate_act(const sv_act *A) {
     SV_REQUIRE(A->M >= 1 && A->M <= SV_MAX_M, SV_ERR_ARG, "M must be in [1, 16]");
     SV_REQUIRE(A->q && A->d && A->s16, SV_ERR_ARG, "activation buffers must not be NULL");
     SV_REQUIRE(A->K > 0 && A->K % 32 == 0 && A->K <= kMaxS * kMaxChunkSteps * 256, SV_ERR_SHAPE,
-               "activation K must be a positive multiple of 32, at most 24576");
+               "activation K must be a positive multiple of 32, at most 40960");
     SV_REQUIRE(aligned(A->q, 16) && aligned(A->d, 4) && aligned(A->s16, 8), SV_ERR_ALIGN,
                "activation codes must be 16-byte aligned, scales 4-byte, sums 8-byte");
     if (A->sumsq_parts) {
@@ -156,9 +191,11 @@ static int validate_weight(const sv_weight &W, int64_t K) {
     SV_REQUIRE(W.data, SV_ERR_ARG, "weight data is NULL");
     SV_REQUIRE(W.qtype == SV_Q8_0 || W.qtype == SV_Q4_K || W.qtype == SV_Q6_K, SV_ERR_QTYPE,
                "unsupported qtype " + std::to_string(W.qtype));
-    Streams s;
-    SV_REQUIRE(streams_of(W.qtype, W.rows, W.cols, &s), SV_ERR_SHAPE,
+    Blocked L;
+    SV_REQUIRE(blocked_of(W.qtype, W.rows, W.cols, &L), SV_ERR_SHAPE,
                "weight cols must be a multiple of 32 (Q8_0) or 256 (Q4_K, Q6_K)");
+    SV_REQUIRE(L.total - kTailPad < (static_cast<size_t>(1) << 32), SV_ERR_SHAPE,
+               "a repacked matrix must stay under 4 GiB");
     SV_REQUIRE(W.cols == K, SV_ERR_SHAPE, "weight cols must equal the activation K");
     SV_REQUIRE(W.rows < (1ll << 31), SV_ERR_SHAPE, "weight rows must be < 2^31");
     SV_REQUIRE(aligned(W.data, 256), SV_ERR_ALIGN, "repacked weights must be 256-byte aligned");
@@ -167,7 +204,8 @@ static int validate_weight(const sv_weight &W, int64_t K) {
 
 // Fill a PhaseDesc from ABI arguments (no scratch pointers yet).
 static int make_phase(PhaseDesc &P, const sv_weight *W, int32_t n_w, const sv_act *A, float *const *y,
-                      const sv_epilogue *ep, const int32_t *row_ids, int64_t n_rows, uint64_t *argmax) {
+                      const sv_epilogue *ep, const int32_t *row_ids, int64_t n_rows, uint64_t *argmax,
+                      bool balance) {
     SV_REQUIRE(W, SV_ERR_ARG, "weights are NULL");
     SV_REQUIRE(n_w >= 1 && n_w <= 3, SV_ERR_ARG, "n_w must be 1..3");
     int rc = validate_act(A);
@@ -187,11 +225,7 @@ static int make_phase(PhaseDesc &P, const sv_weight *W, int32_t n_w, const sv_ac
     P.N = static_cast<int32_t>(row_ids ? n_rows : W[0].rows);
     P.K = static_cast<int32_t>(A->K);
     P.M = A->M;
-    Streams s;
-    streams_of(W[0].qtype, W[0].rows, W[0].cols, &s);
-    P.o1 = s.off[1];
-    P.o2 = s.off[2];
-    P.o3 = s.off[3];
+    P.bbytes = block_bytes(W[0].qtype);
     for (int i = 0; i < n_w; i++) {
         P.w[i] = static_cast<const uint8_t *>(W[i].data);
         P.y[i] = y ? y[i] : nullptr;
@@ -226,7 +260,7 @@ static int make_phase(PhaseDesc &P, const sv_weight *W, int32_t n_w, const sv_ac
         P.os16 = ep->s16;
         P.osumsq = ep->sumsq;
     }
-    decompose(P);
+    decompose(P, balance);
     return SV_OK;
 }
 
@@ -270,11 +304,11 @@ __global__ void zero_u64(unsigned long long *p, int n) {
 // ----------------------------------------------------------------- ABI
 extern "C" size_t sv_matvec_workspace_bytes(const sv_weight *W, int32_t n_w, const sv_act *A) {
     sv::PhaseDesc P;
-    if (sv::make_phase(P, W, n_w, A, nullptr, nullptr, nullptr, 0, nullptr) != SV_OK) return 0;
+    if (sv::make_phase(P, W, n_w, A, nullptr, nullptr, nullptr, 0, nullptr, true) != SV_OK) return 0;
     // sized for any epilogue: two matrices may be paired
     if (n_w == 2) {
         P.ep_mode = SV_EP_PAIR;
-        sv::decompose(P);
+        sv::decompose(P, true);
     }
     return sv::phase_scratch(P, A->M);
 }
@@ -282,17 +316,17 @@ extern "C" size_t sv_matvec_workspace_bytes(const sv_weight *W, int32_t n_w, con
 extern "C" int sv_verify_matvec(const sv_weight *W, int32_t n_w, const sv_act *A, float *const *y,
                                 const sv_epilogue *ep, void *workspace, size_t ws_bytes, void *stream) {
     sv::PhaseDesc P;
-    int rc = sv::make_phase(P, W, n_w, A, y, ep, nullptr, 0, nullptr);
+    int rc = sv::make_phase(P, W, n_w, A, y, ep, nullptr, 0, nullptr, true);
     if (rc) return rc;
     return sv::launch_single(P, A->M, workspace, ws_bytes, sv::as_stream(stream));
 }
 
 extern "C" size_t sv_head_workspace_bytes(const sv_weight *H, const sv_act *A, int64_t n_rows) {
     sv::PhaseDesc P;
-    if (sv::make_phase(P, H, 1, A, nullptr, nullptr, nullptr, 0, nullptr) != SV_OK) return 0;
+    if (sv::make_phase(P, H, 1, A, nullptr, nullptr, nullptr, 0, nullptr, false) != SV_OK) return 0;
     if (n_rows > 0) {
         P.N = static_cast<int32_t>(n_rows);
-        sv::decompose(P);
+        sv::decompose(P, false);
     }
     return sv::phase_scratch(P, A->M);
 }
@@ -309,7 +343,7 @@ extern "C" int sv_head_logits(const sv_weight *H, const sv_act *A, const int32_t
     SV_REQUIRE(!row_ids || aligned(row_ids, 4), SV_ERR_ALIGN, "head_logits: row_ids must be 4-byte aligned");
     float *ys[1] = {logits};
     PhaseDesc P;
-    int rc = make_phase(P, H, 1, A, ys, nullptr, row_ids, n_rows, argmax);
+    int rc = make_phase(P, H, 1, A, ys, nullptr, row_ids, n_rows, argmax, false);
     if (rc) return rc;
     hipStream_t st = as_stream(stream);
     if (argmax) {
@@ -351,8 +385,10 @@ static int plan_pass(const sv_phase *phases, int32_t n_phases, std::vector<Phase
     size_t scratch = 0;
     for (int i = 0; i < n_phases; i++) {
         const sv_phase &ph = phases[i];
+        // a head phase (row gather or argmax) is cut as sv_head_logits cuts
+        // it, every other phase as sv_verify_matvec does
         int rc = make_phase(host[i], ph.W, ph.n_w, &ph.A, ph.y, ph.ep.mode ? &ph.ep : nullptr, ph.row_ids, ph.n_rows,
-                            ph.argmax);
+                            ph.argmax, !(ph.row_ids || ph.argmax));
         if (rc) return fail(rc, "pass: phase " + std::to_string(i) + ": " + std::string(sv_last_error()));
         SV_REQUIRE(ph.A.M == phases[0].A.M, SV_ERR_SHAPE, "pass: all phases need the same M");
         if (needs_partials(host[i])) {
@@ -488,8 +524,12 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
         // The readers of a phase read only its requantised output: with K
         // unsplit and no pairing, that comes from the units of matrix
         // ep_src alone.
-        P.count_all = (P.S > 1 || P.ep_mode != SV_EP_QUANT) ? 1 : 0;
+        P.count_all = (P.S1 > 1 || P.ep_mode != SV_EP_QUANT) ? 1 : 0;
         P.ready = readers[i] ? ctl + kSlotStride * (1 + i * kPhaseCounters) : nullptr;
+        // a phase whose last round is cut finer starts on workgroup 0 of a
+        // round, so the finer chunk each workgroup gets lies inside the
+        // chunk it staged for its earlier units of the phase
+        if (P.T1 < P.n_tiles) tickets = (tickets + kBalanceGrid - 1) / kBalanceGrid * kBalanceGrid;
         P.unit_base = tickets;
         tickets += static_cast<uint32_t>(P.n_units);
         if (P.argmax) {

@@ -107,21 +107,43 @@ __device__ __forceinline__ void unit_next(const Tab &tab, int n_phases, uint32_t
     unit_seek(tab, n_phases, b, G, c);
 }
 
-// Geometry of a unit: tile, K chunk and matrix; the chunk's steps [c0, c1)
-// and its staged sub-blocks [s_begin, s_begin + cs).
+// Geometry of a unit: tile, K chunk (of the tile's nch) and matrix; the
+// chunk's steps [c0, c1) and its sub-blocks [s_begin, s_begin + cs).
+// Units [0, T1 per_tile) are the tiles cut into S chunks, tile-major, then
+// matrix, then chunk.  The rest are the tiles cut into S1 = f S chunks,
+// ordered so that, with the phase starting on a round, the workgroup that
+// ran chunk c of the first kind (unit index = c mod S, matrix likewise) gets
+// one of the f finer chunks inside chunk c.
 struct UnitPos {
-    int tile, chunk, mat, c0, c1, s_begin, cs;
+    int tile, chunk, nch, mat, c0, c1, s_begin, cs;
 };
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, uint32_t m, uint32_t sh) {
+    return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> sh);
+}
 template <class PD>
 __device__ __forceinline__ UnitPos unit_pos(const PD &P, uint32_t u) {
     UnitPos g;
-    const int per_tile = P.per_tile, S = P.S, steps = P.steps;
-    g.tile = static_cast<int>(u) / per_tile;
-    const int rem = static_cast<int>(u) % per_tile;
-    g.chunk = rem % S;
-    g.mat = rem / S;
-    g.c0 = g.chunk * steps / S;
-    g.c1 = (g.chunk + 1) * steps / S;
+    const uint32_t per_tile = P.per_tile, S = P.S, steps = P.steps;
+    const uint32_t head = static_cast<uint32_t>(P.T1) * per_tile;
+    const bool tail = u >= head;
+    const uint32_t v = tail ? u - head : u;
+    const uint32_t q = fdiv(v, P.div_pt.m, P.div_pt.sh), rem = v - q * per_tile;
+    const uint32_t mat = fdiv(rem, P.div_S.m, P.div_S.sh), c = rem - mat * S;
+    g.mat = static_cast<int>(mat);
+    uint32_t nch = S, chunk = c, tile = q;
+    if (tail) {
+        const uint32_t f = fdiv(static_cast<uint32_t>(P.S1), P.div_S.m, P.div_S.sh);
+        const uint32_t qf = fdiv(q, P.div_f.m, P.div_f.sh);
+        chunk = f * c + (q - qf * f);
+        tile = static_cast<uint32_t>(P.T1) + qf;
+        nch = P.S1;
+    }
+    g.tile = static_cast<int>(tile);
+    g.chunk = static_cast<int>(chunk);
+    g.nch = static_cast<int>(nch);
+    const uint32_t dm = tail ? P.div_S1.m : P.div_S.m, ds = tail ? P.div_S1.sh : P.div_S.sh;
+    g.c0 = static_cast<int>(fdiv(chunk * steps, dm, ds));
+    g.c1 = static_cast<int>(fdiv((chunk + 1) * steps, dm, ds));
     const int nsub = P.K >> 5;
     g.s_begin = g.c0 * 8;
     g.cs = min((g.c1 - g.c0) * 8, nsub - g.s_begin);
@@ -142,7 +164,7 @@ __device__ __forceinline__ WaveSpan wave_span(const PD &P, const UnitPos &g, int
     s.w1 = g.c0 + (part + 1) * tc / kStepParts;
     s.sp = P.qtype == SV_Q4_K ? 2 : 1;
     // a fused pair alternates gate and up items over the same steps
-    s.nitems = max(1, (s.w1 - s.w0 + s.sp - 1) / s.sp) * (P.fused ? 2 : 1);
+    s.nitems = max(1, (s.w1 - s.w0 + s.sp - 1) >> (s.sp - 1)) * (P.fused ? 2 : 1);
     return s;
 }
 
@@ -172,19 +194,21 @@ struct WRaw<SV_Q6_K> {
 // One item of the ring: the raw records of a lane in named registers (every
 // index below is a template parameter, so nothing is ever addressed by a
 // runtime index, which would put the ring in memory).  An item is always the
-// same twelve loads into the same registers, four of 16 bytes (quads q0-q3)
-// and eight of 2 bytes (half-words h0-h7); only their addresses depend on
-// the format.  So the loads in flight never depend on the path taken, and
-// the compiler's wait before a slot is read covers that slot alone.
-//   Q4_K (record i = 2 step + row, or for a pair 2 matrix + row): quants in
-//        quad i, the lane's header dword in h(2i) | h(2i + 1) << 16
+// same eight loads into the same registers, four of 16 bytes (quads q0-q3)
+// and four of 4 bytes (words x0-x3); only their addresses depend on the
+// format.  So the loads in flight never depend on the path taken, and the
+// compiler's wait before a slot is read covers that slot alone.
+//   Q4_K (record i = 2 step + row): quants in quad i, the lane's header
+//        dword (lane & 3) in word i
 //   Q6_K (row p < 2): low nibbles in quad p, high bits in the first 8 bytes
-//        of quad 2 + p, the two int8 sub-scales in h(p), d in h(2 + p)
-//   Q8_0 (row p < 2): quants in quads 2p and 2p + 1, d in h(p)
-// Half-words a format does not use repeat an earlier address.
+//        of quad 2 + p, the two int8 sub-scales in word p, d in word 2 + p
+//   Q8_0 (row p < 2): quants in quads 2p and 2p + 1, d in word p
+// (a Q6_K or Q8_0 word is the dword of the row's pair; the row's 2 bytes
+// are its half hs[p] / 16)
+// Words a format does not use repeat an earlier address.
 struct Slot {
     uint4 q0, q1, q2, q3;
-    uint32_t h0, h1, h2, h3, h4, h5, h6, h7;
+    uint32_t x0, x1, x2, x3;
 };
 
 template <int I>
@@ -195,33 +219,29 @@ __device__ __forceinline__ const uint4 &quad(const Slot &s) {
     else return s.q3;
 }
 template <int I>
-__device__ __forceinline__ uint32_t half(const Slot &s) {
-    if constexpr (I == 0) return s.h0;
-    else if constexpr (I == 1) return s.h1;
-    else if constexpr (I == 2) return s.h2;
-    else if constexpr (I == 3) return s.h3;
-    else if constexpr (I == 4) return s.h4;
-    else if constexpr (I == 5) return s.h5;
-    else if constexpr (I == 6) return s.h6;
-    else return s.h7;
+__device__ __forceinline__ uint32_t word(const Slot &s) {
+    if constexpr (I == 0) return s.x0;
+    else if constexpr (I == 1) return s.x1;
+    else if constexpr (I == 2) return s.x2;
+    else return s.x3;
 }
 
 template <int QT, int I>
-__device__ __forceinline__ WRaw<QT> rec_of(const Slot &s) {
+__device__ __forceinline__ WRaw<QT> rec_of(const Slot &s, uint32_t hs) {
     WRaw<QT> r;
     if constexpr (QT == SV_Q8_0) {
         r.q0 = quad<2 * I>(s);
         r.q1 = quad<2 * I + 1>(s);
-        r.d = half<I>(s);
+        r.d = word<I>(s) >> hs;
     } else if constexpr (QT == SV_Q4_K) {
         r.q = quad<I>(s);
-        r.h = half<2 * I>(s) | (half<2 * I + 1>(s) << 16);
+        r.h = word<I>(s);
     } else {
         r.l = quad<I>(s);
         const uint4 hq = quad<2 + I>(s);
         r.h = make_uint2(hq.x, hq.y);
-        r.sc = half<I>(s);
-        r.d = half<2 + I>(s);
+        r.sc = word<I>(s) >> hs;
+        r.d = word<2 + I>(s) >> hs;
     }
     return r;
 }
@@ -348,10 +368,11 @@ struct ActLds {
     const uint8_t *q;
     const float *d;
     const int2 *x;
-    int cs;
+    int cs, begin;   // staged sub-blocks [begin, begin + cs) of K
 };
-__device__ __forceinline__ ActLds act_lds(const uint8_t *act, int M, int cs) {
+__device__ __forceinline__ ActLds act_lds(const uint8_t *act, int M, int cs, int begin) {
     ActLds a;
+    a.begin = begin;
     a.q = act;
     a.d = reinterpret_cast<const float *>(act + M * cs * 32);
     a.x = reinterpret_cast<const int2 *>(act + M * cs * 36);
@@ -452,6 +473,7 @@ struct Shared {
     float rscale[SV_MAX_M];
     unsigned long long best[SV_MAX_M];
     unsigned abort;
+    int stb, stc;   // staged sub-blocks [stb, stb + stc), published before B1
 };
 
 // Dynamic LDS: wave partials [2 buffers][8 waves][2 matrices][M][16 rows]
@@ -481,13 +503,17 @@ struct ItemCur {
     const uint8_t *w0, *w1, *w2;
     const uint8_t *wm;   // matrix of the current unit
     int qtype, fused, K, N, wrows;
-    uint64_t o1, o2, o3;
+    uint32_t bbytes;   // bytes of a weight block
+    uint32_t fsh;      // 1 for a fused pair (items alternate matrices), else 0
+    uint32_t sp;       // steps per item (2 for Q4_K)
+    uint32_t last;     // the last step an item of this wave may read
     const int32_t *row_ids;
     // unit
     UnitPos g;
     WaveSpan s;
-    bool sync;        // a barrier opens this unit (new phase or new chunk)
-    int64_t srow[2];  // rows this lane reads (load cursor only)
+    bool newphase;    // the unit opens a phase (a barrier opens it)
+    uint32_t off[8];  // this lane's byte offsets of the unit's eight loads (load cursor only)
+    uint32_t hs[2];   // 16 x (row & 1) of this lane's two rows (compute cursor only)
 };
 
 template <class Tab>
@@ -501,16 +527,16 @@ __device__ __forceinline__ void cur_phase(const Tab &tab, ItemCur &c) {
     c.K = P.K;
     c.N = P.N;
     c.wrows = P.wrows;
-    c.o1 = P.o1;
-    c.o2 = P.o2;
-    c.o3 = P.o3;
+    c.bbytes = P.bbytes;
+    c.fsh = static_cast<uint32_t>(P.fused);
+    c.sp = P.qtype == SV_Q4_K ? 2u : 1u;
     c.row_ids = P.row_ids;
 }
 
 // Rows of this lane in the unit: 2 grp + p of the wave's half tile, mapped
 // through row_ids (read with scalar loads, so they never wait on the ring's
 // weight records) and clamped into the matrix.
-__device__ __forceinline__ void cur_rows(ItemCur &c, int wave) {
+__device__ __forceinline__ void lane_rows(const ItemCur &c, int wave, int32_t (&rho)[2]) {
     const int lane = threadIdx.x & 63, grp = lane >> 3;
     const int64_t rw = static_cast<int64_t>(c.g.tile) * kRows + 16 * (wave & 1);
     if (c.row_ids) {
@@ -527,25 +553,84 @@ __device__ __forceinline__ void cur_rows(ItemCur &c, int wave) {
 #pragma unroll
             for (int k = 1; k < 8; k++)
                 if (grp == k) v = id[2 * k + p];
-            c.srow[p] = (v < 0 || v >= c.wrows) ? 0 : v;
+            rho[p] = (v < 0 || v >= c.wrows) ? 0 : v;
         }
     } else {
+        // rows of the last half tile past the matrix are zero in the layout;
+        // a half tile wholly past it reads row 0 (its outputs are dropped)
+        const int64_t padded = ((static_cast<int64_t>(c.wrows) + 15) >> 4) << 4;
 #pragma unroll
         for (int p = 0; p < 2; p++) {
             const int64_t r = rw + grp * 2 + p;
-            c.srow[p] = r < c.N ? r : 0;
+            rho[p] = static_cast<int32_t>(r < padded ? r : 0);
         }
     }
 }
 
+// The compute cursor needs only which half of a pair dword holds each row.
+__device__ __forceinline__ void cur_shifts(ItemCur &c, int wave) {
+    if (c.row_ids) {
+        int32_t rho[2];
+        lane_rows(c, wave, rho);
+        c.hs[0] = static_cast<uint32_t>(rho[0] & 1) * 16u;
+        c.hs[1] = static_cast<uint32_t>(rho[1] & 1) * 16u;
+    } else {
+        c.hs[0] = 0u;    // rows 2 g and 2 g + 1 of the half tile
+        c.hs[1] = 16u;
+    }
+}
+
+__device__ __forceinline__ void cur_rows(ItemCur &c, int wave) {
+    const int lane = threadIdx.x & 63, jl = lane & 7;
+    int32_t rho[2];
+    lane_rows(c, wave, rho);
+    // byte offset of each row's half-tile block column, then of the pieces
+    const uint32_t steps = static_cast<uint32_t>((c.K + 255) >> 8);
+    uint32_t hb[2];
+    int rr[2];
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+        hb[p] = static_cast<uint32_t>(rho[p] >> 4) * steps * c.bbytes;
+        rr[p] = rho[p] & 15;
+    }
+    if (c.qtype == SV_Q4_K) {
+        c.off[0] = hb[0] + blk_q4k_codes(rr[0], jl);
+        c.off[1] = hb[1] + blk_q4k_codes(rr[1], jl);
+        c.off[2] = c.off[0];
+        c.off[3] = c.off[1];
+        c.off[4] = hb[0] + blk_q4k_hdr(rr[0]) + (lane & 3) * 4;
+        c.off[5] = hb[1] + blk_q4k_hdr(rr[1]) + (lane & 3) * 4;
+        c.off[6] = c.off[4];
+        c.off[7] = c.off[5];
+    } else if (c.qtype == SV_Q6_K) {
+        c.off[0] = hb[0] + blk_q6k_ql(rr[0], jl);
+        c.off[1] = hb[1] + blk_q6k_ql(rr[1], jl);
+        c.off[2] = hb[0] + blk_q6k_qh(rr[0], jl);
+        c.off[3] = hb[1] + blk_q6k_qh(rr[1], jl);
+        c.off[4] = hb[0] + blk_q6k_sc(rr[0], jl);
+        c.off[5] = hb[1] + blk_q6k_sc(rr[1], jl);
+        c.off[6] = hb[0] + blk_q6k_d(rr[0]);
+        c.off[7] = hb[1] + blk_q6k_d(rr[1]);
+    } else {
+        c.off[0] = hb[0] + blk_q80_lo(rr[0], jl);
+        c.off[1] = c.off[0] + 1024u;
+        c.off[2] = hb[1] + blk_q80_lo(rr[1], jl);
+        c.off[3] = c.off[2] + 1024u;
+        c.off[4] = hb[0] + blk_q80_d(rr[0], jl);
+        c.off[5] = hb[1] + blk_q80_d(rr[1], jl);
+        c.off[6] = c.off[4];
+        c.off[7] = c.off[5];
+    }
+}
+
 template <class Tab>
-__device__ __forceinline__ void cur_unit(const Tab &tab, ItemCur &c, int wave, bool phase_changed, int prev_chunk,
-                                         bool rows) {
+__device__ __forceinline__ void cur_unit(const Tab &tab, ItemCur &c, int wave, bool phase_changed, bool rows) {
     const auto &P = tab[c.uc.p];
     c.g = unit_pos(P, c.uc.u);
     c.s = wave_span(P, c.g, wave);
+    c.last = static_cast<uint32_t>(max(c.s.w1 - 1, c.g.c0));
     c.item = 0;
-    c.sync = phase_changed || c.g.chunk != prev_chunk;
+    c.newphase = phase_changed;
     // integer arithmetic, not a select: a select among the three fields is
     // turned into an indexed load, which puts the whole cursor in memory
     const uint64_t m0 = c.g.mat == 0, m1 = c.g.mat == 1, m2 = c.g.mat == 2;
@@ -553,6 +638,7 @@ __device__ __forceinline__ void cur_unit(const Tab &tab, ItemCur &c, int wave, b
                                              m1 * reinterpret_cast<uint64_t>(c.w1) +
                                              m2 * reinterpret_cast<uint64_t>(c.w2));
     if (rows) cur_rows(c, wave);
+    else cur_shifts(c, wave);
 }
 
 template <class Tab>
@@ -561,7 +647,7 @@ __device__ __forceinline__ bool cur_init(const Tab &tab, int n_phases, uint32_t 
     unit_first(tab, n_phases, b, G, c.uc);
     if (c.uc.p >= n_phases) return false;
     cur_phase(tab, c);
-    cur_unit(tab, c, wave, true, -1, rows);
+    cur_unit(tab, c, wave, true, rows);
     return true;
 }
 
@@ -570,11 +656,11 @@ template <class Tab>
 __device__ __forceinline__ bool cur_advance(const Tab &tab, int n_phases, uint32_t b, uint32_t G, ItemCur &c,
                                             int wave, bool rows) {
     if (++c.item < c.s.nitems) return true;
-    const int p0 = c.uc.p, chunk0 = c.g.chunk;
+    const int p0 = c.uc.p;
     unit_next(tab, n_phases, b, G, c.uc);
     if (c.uc.p >= n_phases) return false;
     if (c.uc.p != p0) cur_phase(tab, c);
-    cur_unit(tab, c, wave, c.uc.p != p0, chunk0, rows);
+    cur_unit(tab, c, wave, c.uc.p != p0, rows);
     return true;
 }
 
@@ -590,108 +676,53 @@ __device__ __forceinline__ bool cur_advance_keep(const Tab &tab, int n_phases, u
     UnitCur nx = c.uc;
     unit_next(tab, n_phases, b, G, nx);
     if (nx.p >= n_phases) return false;
-    const int p0 = c.uc.p, chunk0 = c.g.chunk;
+    const int p0 = c.uc.p;
     c.uc = nx;
     if (c.uc.p != p0) cur_phase(tab, c);
-    cur_unit(tab, c, wave, c.uc.p != p0, chunk0, rows);
+    cur_unit(tab, c, wave, c.uc.p != p0, rows);
     return true;
 }
 
-// Requests the records of the cursor's item into slot s.  Every item
-// issues the same loads whether or not its steps exist (a missing step reads
-// the chunk's first sub-block again and is never used), so the number of
-// loads in flight does not depend on the data.
-__device__ __forceinline__ int64_t item_sb(const ItemCur &c, int t, int64_t fallback) {
-    const int64_t nsub = c.K >> 5;
-    const int64_t sb = static_cast<int64_t>(t) * 8 + (threadIdx.x & 7);
-    return (t < c.s.w1 && sb < nsub) ? sb : fallback;
-}
-
+// Requests the records of the cursor's item into slot s: eight loads at a
+// wave-uniform block address (scalar registers) plus the lane's offsets of
+// the unit.  Every item issues the same loads whether or not its steps
+// exist (a step past the wave's span reads the last step of the span again,
+// or the chunk's first step for an empty span, and is never used), so the
+// number of loads in flight does not depend on the data.
 __device__ __forceinline__ uint4 q16(const uint8_t *p) { return gld16_nt(p); }
-__device__ __forceinline__ uint32_t h2(const uint8_t *p) { return gld(reinterpret_cast<const uint16_t *>(p)); }
+__device__ __forceinline__ uint32_t w4(const uint8_t *p) { return gld(reinterpret_cast<const uint32_t *>(p)); }
 
 __device__ __forceinline__ void load_item(Slot &s, const ItemCur &c) {
-    const int jl = threadIdx.x & 7;
-    const int64_t r0 = c.srow[0], r1 = c.srow[1];
-    const int64_t K = c.K, nsub = K >> 5, nsb = K >> 8;
-    const bool q4 = c.qtype == SV_Q4_K;
-    // a fused pair's item 2k is gate, 2k + 1 up, over the same steps
-    const int it = c.fused ? (c.item >> 1) : c.item;
-    const uint64_t odd = c.fused ? static_cast<uint64_t>(c.item & 1) : 0u;
-    const uint8_t *wsel = reinterpret_cast<const uint8_t *>((1u - odd) * reinterpret_cast<uint64_t>(c.wm) +
-                                                            odd * reinterpret_cast<uint64_t>(c.w1));
-    const int t = c.s.w0 + it * (q4 ? 2 : 1);
-    const int64_t fb = c.g.s_begin + (c.qtype == SV_Q8_0 ? 0 : jl);
-    const int64_t sa = item_sb(c, t, fb);
-    const int64_t sb = q4 ? item_sb(c, t + 1, fb) : sa;
-    const uint8_t *a0, *a1, *a2, *a3, *b0, *b1, *b2, *b3, *b4, *b5, *b6, *b7;
-    if (q4) {
-        // records: (r0, sa), (r1, sa), (r0, sb), (r1, sb)
-        const uint8_t *w = wsel;
-        a0 = w + (r0 * nsub + sa) * 16;
-        a1 = w + (r1 * nsub + sa) * 16;
-        a2 = w + (r0 * nsub + sb) * 16;
-        a3 = w + (r1 * nsub + sb) * 16;
-        const int64_t lh = (sa & 3) * 4, lh2 = (sb & 3) * 4;
-        b0 = w + c.o1 + (r0 * nsb + (sa >> 3)) * 16 + lh;
-        b2 = w + c.o1 + (r1 * nsb + (sa >> 3)) * 16 + lh;
-        b4 = w + c.o1 + (r0 * nsb + (sb >> 3)) * 16 + lh2;
-        b6 = w + c.o1 + (r1 * nsb + (sb >> 3)) * 16 + lh2;
-        b1 = b0 + 2;
-        b3 = b2 + 2;
-        b5 = b4 + 2;
-        b7 = b6 + 2;
-    } else if (c.qtype == SV_Q6_K) {
-        a0 = wsel + (r0 * nsub + sa) * 16;
-        a1 = wsel + (r1 * nsub + sa) * 16;
-        // 16 bytes from the 8-byte high-bit record: the stream is followed by
-        // the scale streams, so the extra 8 bytes stay inside the matrix
-        a2 = wsel + c.o1 + (r0 * nsub + sa) * 8;
-        a3 = wsel + c.o1 + (r1 * nsub + sa) * 8;
-        b0 = wsel + c.o2 + r0 * (K >> 4) + 2 * sa;
-        b1 = wsel + c.o2 + r1 * (K >> 4) + 2 * sa;
-        b2 = wsel + c.o3 + (r0 * nsb + (sa >> 3)) * 2;
-        b3 = wsel + c.o3 + (r1 * nsb + (sa >> 3)) * 2;
-        b4 = b0;
-        b5 = b1;
-        b6 = b2;
-        b7 = b3;
-    } else {
-        a0 = wsel + r0 * K + sa * 32;
-        a1 = a0 + 16;
-        a2 = wsel + r1 * K + sa * 32;
-        a3 = a2 + 16;
-        b0 = wsel + c.o1 + (r0 * nsub + sa) * 2;
-        b1 = wsel + c.o1 + (r1 * nsub + sa) * 2;
-        b2 = b0;
-        b3 = b1;
-        b4 = b0;
-        b5 = b1;
-        b6 = b0;
-        b7 = b1;
-    }
-    s.q0 = q16(a0);
-    s.q1 = q16(a1);
-    s.q2 = q16(a2);
-    s.q3 = q16(a3);
-    s.h0 = h2(b0);
-    s.h1 = h2(b1);
-    s.h2 = h2(b2);
-    s.h3 = h2(b3);
-    s.h4 = h2(b4);
-    s.h5 = h2(b5);
-    s.h6 = h2(b6);
-    s.h7 = h2(b7);
+    // integer arithmetic on wave-uniform fields only (no booleans), so the
+    // block addresses stay in scalar registers: a fused pair's item 2k is
+    // gate, 2k + 1 up, over the same steps
+    const uint32_t item = static_cast<uint32_t>(c.item);
+    const uint32_t it = item >> c.fsh, odd = item & c.fsh;
+    const uint32_t t0 = min(static_cast<uint32_t>(c.s.w0) + it * c.sp, c.last);
+    const uint32_t t1 = min(t0 + c.sp - 1u, c.last);
+    const uint64_t wm = reinterpret_cast<uint64_t>(c.wm), w1 = reinterpret_cast<uint64_t>(c.w1);
+    const uint64_t wsel = wm + static_cast<uint64_t>(odd) * (w1 - wm);
+    const uint8_t *b0 = reinterpret_cast<const uint8_t *>(wsel + static_cast<uint64_t>(t0 * c.bbytes));
+    const uint8_t *b1 = reinterpret_cast<const uint8_t *>(wsel + static_cast<uint64_t>(t1 * c.bbytes));
+    s.q0 = q16(b0 + c.off[0]);
+    s.q1 = q16(b0 + c.off[1]);
+    s.q2 = q16(b1 + c.off[2]);
+    s.q3 = q16(b1 + c.off[3]);
+    s.x0 = w4(b0 + c.off[4]);
+    s.x1 = w4(b0 + c.off[5]);
+    s.x2 = w4(b1 + c.off[6]);
+    s.x3 = w4(b1 + c.off[7]);
 }
 
 // The block terms of one step (sub-block sl of the staged chunk) for the
 // two rows whose records are I0 and I0 + 1 of the slot, into acc[p][*].
 template <int QT, int I0, int M>
-__device__ __forceinline__ void step_terms(const Slot &s, const ActLds &A, int sl, float (&acc)[2][M]) {
+__device__ __forceinline__ void step_terms(const Slot &s, const ActLds &A, int sl, float (&acc)[2][M],
+                                           uint32_t hs0, uint32_t hs1) {
     const int jl = threadIdx.x & 7;
     WDec d0, d1;
-    decode_w<QT>(d0, rec_of<QT, I0>(s), jl);
-    decode_w<QT>(d1, rec_of<QT, I0 + 1>(s), jl);
+    decode_w<QT>(d0, rec_of<QT, I0>(s, hs0), jl);
+    decode_w<QT>(d1, rec_of<QT, I0 + 1>(s, hs1), jl);
 #pragma unroll
     for (int m = 0; m < M; m++) {
         ARec ar;
@@ -707,18 +738,18 @@ template <int M>
 __device__ __forceinline__ void consume(const Slot &s, const ItemCur &c, const ActLds &A, float (&acc)[2][M]) {
     const int jl = threadIdx.x & 7;
     const int64_t nsub = c.K >> 5;
-    const int it = c.fused ? (c.item >> 1) : c.item;
+    const int it = c.item >> c.fsh;
     if (c.qtype == SV_Q4_K) {
         const int t = c.s.w0 + it * 2;
-        if (t < c.s.w1) step_terms<SV_Q4_K, 0, M>(s, A, t * 8 + jl - c.g.s_begin, acc);
-        if (t + 1 < c.s.w1) step_terms<SV_Q4_K, 2, M>(s, A, (t + 1) * 8 + jl - c.g.s_begin, acc);
+        if (t < c.s.w1) step_terms<SV_Q4_K, 0, M>(s, A, t * 8 + jl - A.begin, acc, 0u, 0u);
+        if (t + 1 < c.s.w1) step_terms<SV_Q4_K, 2, M>(s, A, (t + 1) * 8 + jl - A.begin, acc, 0u, 0u);
     } else {
         const int t = c.s.w0 + it;
         const int64_t sb = static_cast<int64_t>(t) * 8 + jl;
         if (t < c.s.w1 && sb < nsub) {
-            const int sl = static_cast<int>(sb) - c.g.s_begin;
-            if (c.qtype == SV_Q6_K) step_terms<SV_Q6_K, 0, M>(s, A, sl, acc);
-            else step_terms<SV_Q8_0, 0, M>(s, A, sl, acc);
+            const int sl = static_cast<int>(sb) - A.begin;
+            if (c.qtype == SV_Q6_K) step_terms<SV_Q6_K, 0, M>(s, A, sl, acc, c.hs[0], c.hs[1]);
+            else step_terms<SV_Q8_0, 0, M>(s, A, sl, acc, c.hs[0], c.hs[1]);
         }
     }
 }
@@ -747,6 +778,7 @@ struct CompState {
     ItemCur L, C;     // load cursor (a ring ahead) and compute cursor
     bool lv, go;      // load cursor not yet past the end; compute cursor valid and no abort
     int buf;          // wave-partial buffer of the current unit
+    int stb, stc;     // staged sub-blocks [stb, stb + stc) (as the control wave published them)
     ActLds A;
     float acc[2][M];              // matrix of the unit (gate of a fused pair)
     float accu[M <= 8 ? 2 : 1][M]; // up of a fused pair (M <= 8 only)
@@ -760,10 +792,18 @@ struct CompState {
 template <int M, class Tab>
 __device__ __forceinline__ void ring_step(const Tab &tab, int n_phases, uint32_t b, uint32_t G, int wave,
                                           uint8_t *smem, Shared<M> &sh, CompState<M> &st, Slot &s) {
-    if (st.go && st.C.item == 0 && st.C.sync) {
+    // B1 opens a unit that starts a phase or whose K range lies outside
+    // the staged one (the control wave takes the same decision)
+    if (st.go && st.C.item == 0 &&
+        (st.C.newphase || st.C.g.s_begin < st.stb || st.C.g.s_begin + st.C.g.cs > st.stb + st.stc)) {
         lds_barrier();   // B1: the unit's input is staged
-        if (sh.abort) st.go = false;
-        else st.A = act_lds(act_base<M>(smem), M, st.C.g.cs);
+        if (sh.abort) {
+            st.go = false;
+        } else {
+            st.stb = sh.stb;
+            st.stc = sh.stc;
+            st.A = act_lds(act_base<M>(smem), M, st.stc, st.stb);
+        }
     }
     if (st.go) {
         if constexpr (M <= 8) {
@@ -803,6 +843,8 @@ __device__ __forceinline__ void compute_waves(const Tab &tab, int n_phases, uint
     st.go = cur_init(tab, n_phases, b, G, st.C, wave, false);
     if (!st.go) return;
     st.buf = 0;
+    st.stb = 0;
+    st.stc = -1;
 #pragma unroll
     for (int p = 0; p < 2; p++)
 #pragma unroll
@@ -1029,26 +1071,33 @@ template <class PD>
 __device__ __forceinline__ float gamma_of(const PD &P, uint32_t u) {
     const float *gamma = P.gamma;
     if (!gamma || P.ep_mode == SV_EP_NONE) return 1.0f;
-    const int64_t row = static_cast<int64_t>(static_cast<int>(u) / P.per_tile) * kRows + (threadIdx.x & 31);
+    const int64_t row = static_cast<int64_t>(unit_pos(P, u).tile) * kRows + (threadIdx.x & 31);
     return row < P.N ? gld(gamma + row) : 1.0f;
 }
 
 // The control wave's part of a unit whose partial sums sit in wave-partial
-// buffer wp: adds the four step quarters of each row in order (for both
-// matrices of a fused pair), then either finishes the tile, or (K split over
+// buffer wp, right after the unit's barrier, in two halves.  finish_issue
+// adds the four step quarters of each row in order (for both matrices of a
+// fused pair), then either writes the tile's outputs, or (K split over
 // units, or a pair whose matrices sit in two units) stores the chunk's
-// values, and the last unit of the tile to arrive adds all chunks in chunk
-// order and finishes it.  Then the unit is handed off if a later phase
-// reads it.
+// values.  finish_complete, for a split tile, counts the chunk in once those
+// stores have landed and, in the tile's last unit to arrive, adds all
+// chunks in chunk order and writes the outputs; then it hands the unit off
+// if a later phase reads it.
 template <int M, class PD>
-__device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float *wp, float g_row, Shared<M> &sh) {
+__device__ __forceinline__ bool unit_split(const PD &P, const UnitPos &g) {
+    return g.nch > 1 || (P.ep_mode == SV_EP_PAIR && !P.fused);
+}
+
+template <int M, class PD>
+__device__ __forceinline__ void finish_issue(const PD &P, uint32_t u, const float *wp, float g_row, Shared<M> &sh,
+                                             unsigned long long *tr) {
+    if (tr && (threadIdx.x & 63) == 0) tr[7] = now();
     const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5, hr = r >> 4, rr = r & 15;
     const UnitPos g = unit_pos(P, u);
     const int64_t row0 = static_cast<int64_t>(g.tile) * kRows;
     const int64_t N = P.N;
     const int nm = P.fused ? 2 : 1;
-    const bool pair = P.ep_mode == SV_EP_PAIR;
-    const bool split = P.S > 1 || (pair && !P.fused);
     // the step quarters of each row, added in order: waves hr, hr + 2, ...
     TileVals<M> v0, v1;
 #pragma unroll
@@ -1064,7 +1113,7 @@ __device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float
         v0.v[k] = a;
         v1.v[k] = c;
     }
-    if (!split) {
+    if (!unit_split<M>(P, g)) {
 #pragma unroll
         for (int k = 0; k < (M + 1) / 2; k++) {
             const float rs = sh.rscale[min(h + 2 * k, M - 1)];
@@ -1081,7 +1130,7 @@ __device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float
         finish_tile<M>(P, row0, v0, e, nm == 2 || g.mat == P.ep_src, g_row, sh);
     } else {
         float *partial = P.partial;
-        const int S = P.S;
+        const int SP = P.S1;   // chunk slots per matrix
 #pragma unroll
         for (int mm = 0; mm < 2; mm++) {
             if (mm < nm) {
@@ -1089,17 +1138,33 @@ __device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float
                 for (int k = 0; k < (M + 1) / 2; k++) {
                     const int m = h + 2 * k;
                     if (m < M && row0 + r < N)
-                        st_dev(partial + ((static_cast<int64_t>(g.mat + mm) * S + g.chunk) * M + m) * N + row0 + r,
+                        st_dev(partial + ((static_cast<int64_t>(g.mat + mm) * SP + g.chunk) * M + m) * N + row0 + r,
                                mm ? v1.v[k] : v0.v[k]);
                 }
             }
         }
+    }
+    if (tr && lane == 0) tr[8] = now();
+}
+
+template <int M, class PD>
+__device__ __forceinline__ void finish_complete(const PD &P, uint32_t u, float g_row, Shared<M> &sh,
+                                                unsigned long long *tr) {
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+    const UnitPos g = unit_pos(P, u);
+    const int64_t row0 = static_cast<int64_t>(g.tile) * kRows;
+    const int64_t N = P.N;
+    const bool pair = P.ep_mode == SV_EP_PAIR;
+    if (unit_split<M>(P, g)) {
+        float *partial = P.partial;
+        const int SP = P.S1, S = g.nch;   // chunk slots per matrix; chunks of this tile
         drain();
+        if (tr && lane == 0) tr[10] = now();
         unsigned *tc = P.tile_count;
         unsigned prev = 0;
         if (lane == 0) prev = add_dev(tc + g.tile, 1u);
         prev = static_cast<unsigned>(__shfl(static_cast<int>(prev), 0, 64));
-        if (prev == static_cast<unsigned>(P.per_tile - 1)) {
+        if (prev == static_cast<unsigned>(S * P.mu - 1)) {
             const int n_w = P.n_w, src = P.ep_src;
             TileVals<M> f0, e;
 #pragma unroll
@@ -1111,7 +1176,7 @@ __device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float
                         const int m = h + 2 * k;
                         float s = 0.0f;
                         if (m < M && row0 + r < N) {
-                            const float *srcp = partial + (static_cast<int64_t>(mt) * S * M + m) * N + row0 + r;
+                            const float *srcp = partial + (static_cast<int64_t>(mt) * SP * M + m) * N + row0 + r;
                             float v[kMaxS];
 #pragma unroll
                             for (int c = 0; c < kMaxS; c++) {
@@ -1145,6 +1210,7 @@ __device__ __forceinline__ void ctrl_finish(const PD &P, uint32_t u, const float
     unsigned *ready = P.ready;
     if (ready && (P.count_all || g.mat == P.ep_src)) {
         drain();
+        if (tr && lane == 0) tr[11] = now();
         if (lane < kReplicas) add_dev(ready + (lane * kSlots + u % kSlots) * kSlotStride, 1u);
     }
 }
@@ -1154,30 +1220,33 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
                                              Shared<M> &sh, unsigned *status, const unsigned *cleared,
                                              unsigned long long *trace) {
     const int lane = threadIdx.x & 63;
+    // The control wave issues first when it competes with the compute waves
+    // for the SIMD and the memory pipeline: its few instructions (staging,
+    // stores, hand-offs) are on the critical path of every phase, and it
+    // sleeps while it waits, so it never starves them.
+    __builtin_amdgcn_s_setprio(3);
     UnitCur c;
     unit_first(tab, n_phases, b, G, c);
-    int pp = -1, pchunk = -1, buf = 0;
-    uint32_t pu = 0;
+    int pp = -1, buf = 0;
     // what is staged: the input codes, the chunk and the partials
     const int8_t *st_q = nullptr;
     const float *st_parts = nullptr;
     int st_begin = -1, st_cs = -1;
     unsigned long long *tr = nullptr;
     unsigned n_units = 0;
-    float g_prev = 1.0f;    // norm weight of the previous unit's epilogue row
     uint8_t *act = act_base<M>(smem);
     while (c.p < n_phases) {
         const auto &P = tab[c.p];
         const UnitPos g = unit_pos(P, c.u);
-        if (pp >= 0) {
-            ctrl_finish<M>(tab[pp], pu, wpart_buf<M>(smem, buf ^ 1), g_prev, sh);
-            if (tr && lane == 0) {
-                if (n_units == 1) tr[4] = now();
-                tr[5] = now();
-            }
-        }
         const bool phase_change = c.p != pp;
-        if (phase_change || g.chunk != pchunk) {
+        // the unit's input is staged if it is the same input and its K range
+        // lies inside the staged one (the compute waves test the range alone:
+        // without a phase change the input is the same)
+        const int8_t *aq = P.aq;
+        const float *parts = P.in_parts;
+        const bool inside = aq == st_q && parts == st_parts && g.s_begin >= st_begin &&
+                            g.s_begin + g.cs <= st_begin + st_cs;
+        if (phase_change || !(g.s_begin >= st_begin && g.s_begin + g.cs <= st_begin + st_cs)) {
             if (phase_change && pp >= 0) flush_best<M>(tab[pp].argmax, sh, cleared, status);
             if (phase_change) {
                 if (tr && lane == 0) tr[6] = n_units;
@@ -1189,9 +1258,7 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
                             (static_cast<unsigned long long>(__builtin_amdgcn_s_getreg(0xF814)) << 32);
                 }
             }
-            const int8_t *aq = P.aq;
-            const float *parts = P.in_parts;
-            if (aq != st_q || parts != st_parts || g.s_begin != st_begin || g.cs != st_cs) {
+            if (!inside) {
                 const unsigned *wt = P.wait;
                 if (wt && !wait_ready(wt, P.wait_target, status)) {
                     if (lane == 0) sh.abort = 1u;
@@ -1205,27 +1272,31 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
                     st_cs = g.cs;
                 }
             }
+            if (lane == 0) {
+                sh.stb = st_begin;
+                sh.stc = st_cs;
+            }
             lds_barrier();   // B1
             if (sh.abort) break;
         }
-        g_prev = gamma_of(P, c.u);   // in flight while the unit computes
+        const float g_cur = gamma_of(P, c.u);   // in flight while the unit computes
         lds_barrier();       // B2: the compute waves have written the unit's partial sums
         if (sh.abort) break;
-        if (tr && lane == 0 && n_units == 0) tr[3] = now();
+        unsigned long long *tf = n_units == 0 ? tr : nullptr;
+        if (tf && lane == 0) tr[3] = now();
+        finish_issue<M>(P, c.u, wpart_buf<M>(smem, buf), g_cur, sh, tf);
+        finish_complete<M>(P, c.u, g_cur, sh, tf);
+        if (tr && lane == 0) {
+            if (tf) tr[4] = now();
+            tr[5] = now();
+        }
         n_units++;
         pp = c.p;
-        pu = c.u;
-        pchunk = g.chunk;
         buf ^= 1;
         unit_next(tab, n_phases, b, G, c);
     }
     if (pp >= 0 && !sh.abort) {
-        ctrl_finish<M>(tab[pp], pu, wpart_buf<M>(smem, buf ^ 1), g_prev, sh);
-        if (tr && lane == 0) {
-            if (n_units == 1) tr[4] = now();
-            tr[5] = now();
-            tr[6] = n_units;
-        }
+        if (tr && lane == 0) tr[6] = n_units;
         flush_best<M>(tab[pp].argmax, sh, cleared, status);
     }
     drain();

@@ -12,7 +12,8 @@ constexpr int kThreads = 576;          // eight compute waves and one control wa
 constexpr int kRows = 32;              // rows per tile: 2 half tiles of 8 groups x 2 rows
 constexpr int kActRec = 32 + 4 + 8;    // LDS bytes per position per staged sub-block (codes, scale, sums)
 constexpr int kMaxChunkSteps = 20;     // most 256-element steps of K one unit covers
-constexpr int kMaxS = 8;               // most K chunks (K <= 24576)
+constexpr int kMaxS = 8;               // most K chunks of a tile (K <= 40960)
+constexpr int kBalanceGrid = 256;      // workgroups a balanced phase is cut for (one per CU)
 constexpr unsigned kSpinLimit = 1u << 22;
 constexpr int kMaxGrid = 1024;         // most workgroups a pass launches
 constexpr int kMaxArgmax = 4;          // most phases of one pass with an argmax
@@ -40,19 +41,34 @@ constexpr int kPhaseCounters = kSlots * kReplicas;   // counter lines per phase
 
 // Trace record of a (workgroup, phase): real-time counter at phase entry,
 // input ready, input staged, first unit computed, first unit done, last
-// unit done; units run; first unit reduced (partials combined), first unit's
-// epilogue written; HW_ID | XCC_ID << 32; unused.
+// unit done; units run; the first unit's finish: entry, outputs written,
+// partial sums drained (split tiles); HW_ID | XCC_ID << 32; the first
+// unit's hand-off drained.
 constexpr int kTraceWords = 12;
+
+// Division by a divisor d >= 1 fixed per phase: n / d = (n * m) >> sh for
+// every n < 2^31, with l = ceil(log2 d), m = ceil(2^(31 + l) / d) and
+// sh = 31 + l (the round-up method of Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994).  The unit geometry is
+// derived with it from scalar registers, instead of the long vector
+// sequence of a general integer division.
+struct FastDiv {
+    uint32_t m, sh;
+};
 
 // Device-side description of one phase.
 struct PhaseDesc {
     const uint8_t *w[3];
     int32_t qtype, n_w, M;
     int32_t N, K, wrows;
-    int32_t S, steps, n_tiles, per_tile, n_units, chunk_sub;
+    // K chunking: tiles [0, T1) are cut into S chunks, tiles [T1, n_tiles)
+    // into S1 (a multiple of S); a unit covers mu matrices' worth of one
+    // (tile, chunk): per_tile = S * mu units per tile of the first kind.
+    int32_t S, S1, T1, mu, steps, n_tiles, per_tile, n_units, chunk_sub;
+    FastDiv div_pt, div_S, div_f, div_S1;   // by per_tile, S, S1 / S and S1
     int32_t count_all;        // 0: only units of matrix ep_src feed a reader
     int32_t fused;            // 1: a unit covers both matrices of a gate/up pair (M <= 8)
-    uint64_t o1, o2, o3;
+    uint32_t bbytes;          // bytes of a weight block (16 rows x 256 columns)
     const int32_t *row_ids;
     const int8_t *aq;
     const float *ad;
@@ -68,7 +84,7 @@ struct PhaseDesc {
     int32_t *os16;
     float *osumsq;
     unsigned long long *argmax;
-    float *partial;           // [n_w][S][M][N] when the tile is split over units
+    float *partial;           // [n_w][S1][M][N] when a tile is split over units
     unsigned *tile_count;     // [n_tiles], zero between calls
     unsigned *ready;          // finished units of this phase (persistent mode; NULL: no reader)
     const unsigned *wait;     // finished units of the input's producer (NULL: input written before)

@@ -1,11 +1,11 @@
 // repack.hip - load-time rearrangement of GGUF blocks (a1) and its inverse.
 //
-// The projection kernels read every weight row as fixed-size, aligned
-// records (16-byte quant records per 32 elements plus small scale streams),
-// so a group of lanes reading consecutive records of one row issues one
-// contiguous, 16-byte-aligned load per lane.  GGUF's own blocks (34, 144 and
-// 210 bytes) are not 16-byte multiples, and Q4_K / Q6_K interleave the
-// nibbles of two 32-element sub-blocks in one byte range.  Values never
+// The projection kernels read the weights of 16 rows by 256 columns as one
+// contiguous block whose fields are stored in the order the lanes read them
+// (the layout is described with blocked_of), so every load instruction of a
+// wave reads one contiguous range.  GGUF's own blocks (34, 144 and 210
+// bytes) are not 16-byte multiples, and Q4_K / Q6_K interleave the nibbles
+// of two 32-element sub-blocks in one byte range.  Values never
 // change: every field is copied, only moved ("Inside OpenJet Engine: making
 // speculative decoding pay", section "One GPU launch for a speculative
 // cycle": Q6_K and Q8_0 weights are rearranged at load time for aligned
@@ -31,54 +31,100 @@ __device__ __forceinline__ uint32_t q6k_hi(const uint8_t *qh, int e) {
     return (qh[32 * h + l] >> (2 * g)) & 3u;
 }
 
-__global__ void repack_q8_0(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t nblocks,
-                            size_t off_d) {
-    for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblocks;
-         bi += (int64_t)gridDim.x * blockDim.x) {
-        const uint8_t *b = src + bi * 34;
-        uint8_t *q = dst + bi * 32;
-        for (int i = 0; i < 32; i++) q[i] = b[2 + i];
-        dst[off_d + bi * 2] = b[0];
-        dst[off_d + bi * 2 + 1] = b[1];
-    }
+// One thread per (row, step) of the padded matrix: the row's pieces of the
+// block (row >> 4, step) are written from the GGUF super-block (or the 8
+// Q8_0 blocks) of that row and step; rows past the matrix and Q8_0
+// sub-blocks past K are written as zeros.  The inverse reads them back.
+__device__ __forceinline__ void blk_pos(int64_t i, int64_t steps, int64_t &row, int64_t &step) {
+    row = i / steps;
+    step = i - row * steps;
 }
 
-__global__ void unpack_q8_0(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t nblocks,
-                            size_t off_d) {
-    for (int64_t bi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; bi < nblocks;
-         bi += (int64_t)gridDim.x * blockDim.x) {
-        uint8_t *b = dst + bi * 34;
-        b[0] = src[off_d + bi * 2];
-        b[1] = src[off_d + bi * 2 + 1];
-        for (int i = 0; i < 32; i++) b[2 + i] = src[bi * 32 + i];
-    }
-}
-
-__global__ void repack_q4_k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t nsb,
-                            size_t off_h) {
-    for (int64_t si = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; si < nsb;
-         si += (int64_t)gridDim.x * blockDim.x) {
-        const uint8_t *b = src + si * 144;
-        for (int i = 0; i < 16; i++) dst[off_h + si * 16 + i] = b[i];
-        const uint8_t *qs = b + 16;
+__global__ void repack_q8_0(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t rows,
+                            int64_t cols, int64_t n, int64_t steps) {
+    const int64_t nsub = cols / 32;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t row, st;
+        blk_pos(i, steps, row, st);
+        uint8_t *blk = dst + ((row >> 4) * steps + st) * 4352;
+        const int r = static_cast<int>(row & 15);
         for (int j = 0; j < 8; j++) {
-            uint8_t *rec = dst + (si * 8 + j) * 16;
-            for (int i = 0; i < 16; i++)
-                rec[i] = static_cast<uint8_t>(q4k_nib(qs, 32 * j + i) | (q4k_nib(qs, 32 * j + 16 + i) << 4));
+            const int64_t s = st * 8 + j;
+            const bool ok = row < rows && s < nsub;
+            // rows and blocks past the matrix read block 0 (always valid) and write zeros
+            const uint8_t *b = ok ? src + (row * nsub + s) * 34 : src;
+            uint8_t *lo = blk + blk_q80_lo(r, j);
+            for (int k = 0; k < 16; k++) {
+                lo[k] = ok ? b[2 + k] : 0;
+                lo[1024 + k] = ok ? b[18 + k] : 0;
+            }
+            uint8_t *d = blk + blk_q80_d(r, j) + (r & 1) * 2;
+            d[0] = ok ? b[0] : 0;
+            d[1] = ok ? b[1] : 0;
         }
     }
 }
 
-__global__ void unpack_q4_k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t nsb,
-                            size_t off_h) {
-    for (int64_t si = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; si < nsb;
-         si += (int64_t)gridDim.x * blockDim.x) {
-        uint8_t *b = dst + si * 144;
-        for (int i = 0; i < 16; i++) b[i] = src[off_h + si * 16 + i];
+__global__ void unpack_q8_0(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t rows,
+                            int64_t cols, int64_t n, int64_t steps) {
+    const int64_t nsub = cols / 32;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t row, st;
+        blk_pos(i, steps, row, st);
+        if (row >= rows) continue;
+        const uint8_t *blk = src + ((row >> 4) * steps + st) * 4352;
+        const int r = static_cast<int>(row & 15);
+        for (int j = 0; j < 8; j++) {
+            const int64_t s = st * 8 + j;
+            if (s >= nsub) break;
+            uint8_t *b = dst + (row * nsub + s) * 34;
+            const uint8_t *lo = blk + blk_q80_lo(r, j);
+            for (int k = 0; k < 16; k++) {
+                b[2 + k] = lo[k];
+                b[18 + k] = lo[1024 + k];
+            }
+            const uint8_t *d = blk + blk_q80_d(r, j) + (r & 1) * 2;
+            b[0] = d[0];
+            b[1] = d[1];
+        }
+    }
+}
+
+__global__ void repack_q4_k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t rows,
+                            int64_t n, int64_t steps) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t row, st;
+        blk_pos(i, steps, row, st);
+        uint8_t *blk = dst + ((row >> 4) * steps + st) * 2304;
+        const int r = static_cast<int>(row & 15);
+        const bool ok = row < rows;
+        const uint8_t *b = ok ? src + (row * steps + st) * 144 : src;
+        uint8_t *h = blk + blk_q4k_hdr(r);
+        for (int k = 0; k < 16; k++) h[k] = ok ? b[k] : 0;
+        const uint8_t *qs = b + 16;
+        for (int j = 0; j < 8; j++) {
+            uint8_t *rec = blk + blk_q4k_codes(r, j);
+            for (int k = 0; k < 16; k++)
+                rec[k] = ok ? static_cast<uint8_t>(q4k_nib(qs, 32 * j + k) | (q4k_nib(qs, 32 * j + 16 + k) << 4)) : 0;
+        }
+    }
+}
+
+__global__ void unpack_q4_k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t rows,
+                            int64_t n, int64_t steps) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t row, st;
+        blk_pos(i, steps, row, st);
+        if (row >= rows) continue;
+        const uint8_t *blk = src + ((row >> 4) * steps + st) * 2304;
+        const int r = static_cast<int>(row & 15);
+        uint8_t *b = dst + (row * steps + st) * 144;
+        const uint8_t *h = blk + blk_q4k_hdr(r);
+        for (int k = 0; k < 16; k++) b[k] = h[k];
         auto nib = [&](int e) -> uint32_t {
-            const uint8_t *rec = src + (si * 8 + (e >> 5)) * 16;
-            int i = e & 31;
-            return (i < 16) ? (rec[i] & 15u) : (rec[i - 16] >> 4);
+            const uint8_t *rec = blk + blk_q4k_codes(r, e >> 5);
+            const int k = e & 31;
+            return (k < 16) ? (rec[k] & 15u) : (rec[k - 16] >> 4);
         };
         for (int c = 0; c < 4; c++)
             for (int l = 0; l < 32; l++)
@@ -86,51 +132,71 @@ __global__ void unpack_q4_k(const uint8_t *__restrict__ src, uint8_t *__restrict
     }
 }
 
-__global__ void repack_q6_k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t nsb,
-                            size_t off_h, size_t off_s, size_t off_d) {
-    for (int64_t si = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; si < nsb;
-         si += (int64_t)gridDim.x * blockDim.x) {
-        const uint8_t *b = src + si * 210;
+__global__ void repack_q6_k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t rows,
+                            int64_t n, int64_t steps) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t row, st;
+        blk_pos(i, steps, row, st);
+        uint8_t *blk = dst + ((row >> 4) * steps + st) * 3360;
+        const int r = static_cast<int>(row & 15);
+        const bool ok = row < rows;
+        const uint8_t *b = ok ? src + (row * steps + st) * 210 : src;
         const uint8_t *ql = b, *qh = b + 128;
-        for (int bb = 0; bb < 8; bb++) {
-            uint8_t *L = dst + (si * 8 + bb) * 16;
-            for (int i = 0; i < 16; i++)
-                L[i] = static_cast<uint8_t>(q6k_lo(ql, 32 * bb + i) | (q6k_lo(ql, 32 * bb + 16 + i) << 4));
-            uint8_t *H = dst + off_h + (si * 8 + bb) * 8;
+        for (int j = 0; j < 8; j++) {
+            uint8_t *L = blk + blk_q6k_ql(r, j);
+            for (int k = 0; k < 16; k++)
+                L[k] = ok ? static_cast<uint8_t>(q6k_lo(ql, 32 * j + k) | (q6k_lo(ql, 32 * j + 16 + k) << 4)) : 0;
+            uint8_t *H = blk + blk_q6k_qh(r, j);
             for (int hh = 0; hh < 2; hh++)
-                for (int i = 0; i < 4; i++) {
+                for (int k = 0; k < 4; k++) {
                     uint32_t v = 0;
-                    for (int t = 0; t < 4; t++) v |= q6k_hi(qh, 32 * bb + 16 * hh + 4 * t + i) << (2 * t);
-                    H[4 * hh + i] = static_cast<uint8_t>(v);
+                    for (int s = 0; s < 4; s++) v |= q6k_hi(qh, 32 * j + 16 * hh + 4 * s + k) << (2 * s);
+                    H[4 * hh + k] = ok ? static_cast<uint8_t>(v) : 0;
                 }
+            uint8_t *S = blk + blk_q6k_sc(r, j) + (r & 1) * 2;
+            S[0] = ok ? b[192 + 2 * j] : 0;
+            S[1] = ok ? b[192 + 2 * j + 1] : 0;
         }
-        for (int k = 0; k < 16; k++) dst[off_s + si * 16 + k] = b[192 + k];
-        dst[off_d + si * 2] = b[208];
-        dst[off_d + si * 2 + 1] = b[209];
+        uint8_t *d = blk + blk_q6k_d(r) + (r & 1) * 2;
+        d[0] = ok ? b[208] : 0;
+        d[1] = ok ? b[209] : 0;
     }
 }
 
-__global__ void unpack_q6_k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t nsb,
-                            size_t off_h, size_t off_s, size_t off_d) {
-    for (int64_t si = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; si < nsb;
-         si += (int64_t)gridDim.x * blockDim.x) {
-        uint8_t *b = dst + si * 210;
-        for (int i = 0; i < 192; i++) b[i] = 0;
+__global__ void unpack_q6_k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t rows,
+                            int64_t n, int64_t steps) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        int64_t row, st;
+        blk_pos(i, steps, row, st);
+        if (row >= rows) continue;
+        const uint8_t *blk = src + ((row >> 4) * steps + st) * 3360;
+        const int r = static_cast<int>(row & 15);
+        uint8_t *b = dst + (row * steps + st) * 210;
+        for (int k = 0; k < 192; k++) b[k] = 0;
         for (int e = 0; e < 256; e++) {
-            int bb = e >> 5, i = e & 31;
-            const uint8_t *L = src + (si * 8 + bb) * 16;
-            uint32_t lo = (i < 16) ? (L[i] & 15u) : (L[i - 16] >> 4);
-            const uint8_t *H = src + off_h + (si * 8 + bb) * 8;
-            int hh = i >> 4, i2 = i & 15, t = i2 >> 2, ii = i2 & 3;
-            uint32_t hi = (H[4 * hh + ii] >> (2 * t)) & 3u;
-            int h = e >> 7, r = e & 127, g = r >> 5, l = r & 31;
+            const int j = e >> 5, k = e & 31;
+            const uint8_t *L = blk + blk_q6k_ql(r, j);
+            const uint32_t lo = (k < 16) ? (L[k] & 15u) : (L[k - 16] >> 4);
+            const uint8_t *H = blk + blk_q6k_qh(r, j);
+            const int hh = k >> 4, k2 = k & 15, s = k2 >> 2, kk = k2 & 3;
+            const uint32_t hi = (H[4 * hh + kk] >> (2 * s)) & 3u;
+            const int h = e >> 7, rr = e & 127, g = rr >> 5, l = rr & 31;
             b[64 * h + l + 32 * (g & 1)] |= static_cast<uint8_t>(lo << (g < 2 ? 0 : 4));
             b[128 + 32 * h + l] |= static_cast<uint8_t>(hi << (2 * g));
         }
-        for (int k = 0; k < 16; k++) b[192 + k] = src[off_s + si * 16 + k];
-        b[208] = src[off_d + si * 2];
-        b[209] = src[off_d + si * 2 + 1];
+        for (int j = 0; j < 8; j++) {
+            const uint8_t *S = blk + blk_q6k_sc(r, j) + (r & 1) * 2;
+            b[192 + 2 * j] = S[0];
+            b[192 + 2 * j + 1] = S[1];
+        }
+        const uint8_t *d = blk + blk_q6k_d(r) + (r & 1) * 2;
+        b[208] = d[0];
+        b[209] = d[1];
     }
+}
+
+__global__ void zero_tail(uint8_t *p, int n) {
+    if (static_cast<int>(threadIdx.x) < n) p[threadIdx.x] = 0;
 }
 
 static int repack_common(int32_t qtype, const void *src, void *dst, int64_t rows, int64_t cols, void *stream,
@@ -138,32 +204,36 @@ static int repack_common(int32_t qtype, const void *src, void *dst, int64_t rows
     SV_REQUIRE(src && dst, SV_ERR_ARG, "repack: NULL buffer");
     SV_REQUIRE(qtype == SV_Q8_0 || qtype == SV_Q4_K || qtype == SV_Q6_K, SV_ERR_QTYPE,
                "repack: unsupported qtype " + std::to_string(qtype));
-    Streams s;
-    SV_REQUIRE(streams_of(qtype, rows, cols, &s), SV_ERR_SHAPE,
+    Blocked L;
+    SV_REQUIRE(blocked_of(qtype, rows, cols, &L), SV_ERR_SHAPE,
                "repack: cols must be a multiple of 32 (Q8_0) or 256 (Q4_K, Q6_K) and rows > 0");
+    SV_REQUIRE(L.total - kTailPad < (static_cast<size_t>(1) << 32), SV_ERR_SHAPE,
+               "repack: a repacked matrix must stay under 4 GiB");
     SV_REQUIRE(aligned(forward ? dst : src, 256), SV_ERR_ALIGN, "repack: repacked buffer must be 256-byte aligned");
+    const size_t gguf = qtype == SV_Q8_0 ? static_cast<size_t>(rows) * (cols / 32) * 34
+                                         : static_cast<size_t>(rows) * (cols / 256) * (qtype == SV_Q4_K ? 144 : 210);
     const uint8_t *a = static_cast<const uint8_t *>(src);
     uint8_t *b = static_cast<uint8_t *>(dst);
-    SV_REQUIRE(a + s.total <= b || b + s.total <= a, SV_ERR_ARG, "repack: src and dst overlap");
+    const size_t na = forward ? gguf : L.total, nb = forward ? L.total : gguf;
+    SV_REQUIRE(a + na <= b || b + nb <= a, SV_ERR_ARG, "repack: src and dst overlap");
     hipStream_t st = as_stream(stream);
     const int threads = 256;
-    int64_t n = (qtype == SV_Q8_0) ? rows * (cols / 32) : rows * (cols / 256);
-    int64_t blocks64 = (n + threads - 1) / threads;
-    int blocks = static_cast<int>(blocks64 > 65536 ? 65536 : blocks64);
+    const int64_t n = L.hrows * 16 * L.steps;   // (row, step) pairs of the padded matrix
+    const int64_t blocks64 = (n + threads - 1) / threads;
+    const int blocks = static_cast<int>(blocks64 > 65536 ? 65536 : blocks64);
     if (qtype == SV_Q8_0) {
-        if (forward) hipLaunchKernelGGL(repack_q8_0, dim3(blocks), dim3(threads), 0, st, a, b, n, s.off[1]);
-        else hipLaunchKernelGGL(unpack_q8_0, dim3(blocks), dim3(threads), 0, st, a, b, n, s.off[1]);
+        if (forward) hipLaunchKernelGGL(repack_q8_0, dim3(blocks), dim3(threads), 0, st, a, b, rows, cols, n, L.steps);
+        else hipLaunchKernelGGL(unpack_q8_0, dim3(blocks), dim3(threads), 0, st, a, b, rows, cols, n, L.steps);
     } else if (qtype == SV_Q4_K) {
-        if (forward) hipLaunchKernelGGL(repack_q4_k, dim3(blocks), dim3(threads), 0, st, a, b, n, s.off[1]);
-        else hipLaunchKernelGGL(unpack_q4_k, dim3(blocks), dim3(threads), 0, st, a, b, n, s.off[1]);
+        if (forward) hipLaunchKernelGGL(repack_q4_k, dim3(blocks), dim3(threads), 0, st, a, b, rows, n, L.steps);
+        else hipLaunchKernelGGL(unpack_q4_k, dim3(blocks), dim3(threads), 0, st, a, b, rows, n, L.steps);
     } else {
-        if (forward)
-            hipLaunchKernelGGL(repack_q6_k, dim3(blocks), dim3(threads), 0, st, a, b, n, s.off[1], s.off[2],
-                               s.off[3]);
-        else
-            hipLaunchKernelGGL(unpack_q6_k, dim3(blocks), dim3(threads), 0, st, a, b, n, s.off[1], s.off[2],
-                               s.off[3]);
+        if (forward) hipLaunchKernelGGL(repack_q6_k, dim3(blocks), dim3(threads), 0, st, a, b, rows, n, L.steps);
+        else hipLaunchKernelGGL(unpack_q6_k, dim3(blocks), dim3(threads), 0, st, a, b, rows, n, L.steps);
     }
+    if (forward)
+        hipLaunchKernelGGL(zero_tail, dim3(1), dim3(kTailPad), 0, st, b + (L.total - kTailPad),
+                           static_cast<int>(kTailPad));
     return hip_check(hipGetLastError(), "repack launch");
 }
 

@@ -28,12 +28,47 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 // ----------------------------------------------------------------- formats
-// Repacked stream sizes for a rows x cols matrix (bytes of each stream).
-struct Streams {
-    size_t off[4];
-    size_t total;
+// Repacked weights: one block per (half tile of 16 rows, step of 256
+// columns), blocks ordered half tile major, so the rows a wave reads over
+// its steps are one contiguous stretch.  Inside a block every field is
+// stored lane-major: with lane l = 8 g + j reading rows 2 g, 2 g + 1 of the
+// half tile at sub-block j, one load instruction of a field covers one
+// contiguous range.  Rows past the matrix (up to a multiple of 16) and
+// sub-blocks past K (Q8_0, K not a multiple of 256) are zero, and kTailPad
+// zero bytes follow the last block (a load reads up to 8 bytes past a piece).
+// Fields per block, for row r (0..15) of the half tile and sub-block j (a
+// 2-byte field sits in the dword of its row pair, the even row's in the
+// low half, so every small field is read as one aligned dword):
+//   Q4_K (2304 B): 16-byte quant records at (r & 1) 1024 + (r >> 1) 128 +
+//     16 j, the row's 16-byte super-block header at 2048 + 16 r;
+//   Q6_K (3360 B): 16-byte low-nibble records at (r & 1) 1024 + (r >> 1) 128
+//     + 16 j, 8-byte high-bit records at 2048 + (r & 1) 512 + (r >> 1) 64 +
+//     8 j, the two int8 sub-scales in the dword at 3072 + (r >> 1) 32 + 4 j,
+//     fp16 d in the dword at 3328 + (r >> 1) 4;
+//   Q8_0 (4352 B): quant bytes 0-15 at (r & 1) 2048 + (r >> 1) 128 + 16 j,
+//     bytes 16-31 1024 further, fp16 d in the dword at 4096 + (r >> 1) 32 +
+//     4 j.
+constexpr size_t kTailPad = 64;
+struct Blocked {
+    int64_t hrows;    // half tiles (rows rounded up to 16, / 16)
+    int64_t steps;    // 256-column steps (cols rounded up to 256, / 256)
+    uint32_t B;       // bytes per block
+    size_t total;     // hrows * steps * B + kTailPad
 };
-bool streams_of(int32_t qtype, int64_t rows, int64_t cols, Streams *s);
+bool blocked_of(int32_t qtype, int64_t rows, int64_t cols, Blocked *b);
+
+__host__ __device__ inline uint32_t blk_q4k_codes(int r, int j) { return (r & 1) * 1024u + (r >> 1) * 128u + j * 16u; }
+__host__ __device__ inline uint32_t blk_q4k_hdr(int r) { return 2048u + r * 16u; }
+__host__ __device__ inline uint32_t blk_q6k_ql(int r, int j) { return (r & 1) * 1024u + (r >> 1) * 128u + j * 16u; }
+__host__ __device__ inline uint32_t blk_q6k_qh(int r, int j) { return 2048u + (r & 1) * 512u + (r >> 1) * 64u + j * 8u; }
+// dword offsets of the 2-byte fields; the row's half is (r & 1)
+__host__ __device__ inline uint32_t blk_q6k_sc(int r, int j) { return 3072u + (r >> 1) * 32u + j * 4u; }
+__host__ __device__ inline uint32_t blk_q6k_d(int r) { return 3328u + (r >> 1) * 4u; }
+__host__ __device__ inline uint32_t blk_q80_lo(int r, int j) { return (r & 1) * 2048u + (r >> 1) * 128u + j * 16u; }
+__host__ __device__ inline uint32_t blk_q80_d(int r, int j) { return 4096u + (r >> 1) * 32u + j * 4u; }
+__host__ __device__ inline uint32_t block_bytes(int32_t qtype) {
+    return qtype == SV_Q4_K ? 2304u : (qtype == SV_Q6_K ? 3360u : 4352u);
+}
 
 // --------------------------------------------------------- device helpers
 // Global-memory accesses through address-space-1 pointers.  A pointer read

@@ -79,7 +79,7 @@ def upload_weight(qtype, gguf_rows: np.ndarray, K: int):
     N = gguf_rows.shape[0]
     src = dev(gguf_rows.reshape(-1))
     nbytes = sv.repacked_bytes(qtype, N, K)
-    assert nbytes == gguf_rows.size
+    assert gguf_rows.size == sv.gguf_bytes(qtype, N, K)
     dst = t.empty(nbytes + 256, dtype=t.uint8, device="cuda")
     off = (-dst.data_ptr()) % 256
     dst = dst[off:off + nbytes]

@@ -39,11 +39,20 @@ def test_version():
     assert "gfx950" in sv.version()
 
 
+def _blocked(qt, rows, cols):
+    """Tile-blocked size: rows rounded up to 16, cols to 256, one block of
+    16 rows x 256 columns each (the GGUF bytes of those elements), and 64
+    zero bytes after the last block."""
+    per_256 = {8: 8 * 34, 12: 144, 14: 210}[qt]
+    return -(-rows // 16) * 16 * -(-cols // 256) * per_256 + 64
+
+
 @pytest.mark.parametrize("qt,rows,cols,expect", [
-    (8, 1024, 1024, 1024 * 1024 // 32 * 34),
-    (12, 2560, 2560, 2560 * 2560 // 256 * 144),
-    (14, 151936, 5120, 151936 * 5120 // 256 * 210),
-    (14, 5120, 17408, 5120 * 17408 // 256 * 210),
+    (8, 1024, 1024, _blocked(8, 1024, 1024)),
+    (12, 2560, 2560, _blocked(12, 2560, 2560)),
+    (14, 151936, 5120, _blocked(14, 151936, 5120)),
+    (14, 5120, 17408, _blocked(14, 5120, 17408)),
+    (8, 100, 96, _blocked(8, 100, 96)),      # ragged rows and a partial step
     (8, 3, 48, 0),      # cols not a multiple of 32
     (12, 4, 128, 0),    # cols not a multiple of 256
     (3, 4, 256, 0),     # unsupported type
@@ -51,6 +60,10 @@ def test_version():
 ])
 def test_repacked_bytes(qt, rows, cols, expect):
     assert sv.repacked_bytes(qt, rows, cols) == expect
+    if expect:
+        # the blocks hold exactly the GGUF bytes of the padded matrix
+        per_256 = {8: 8 * 34, 12: 144, 14: 210}[qt]
+        assert expect - 64 == -(-rows // 16) * 16 * -(-cols // 256) * per_256
 
 
 FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
@@ -149,24 +162,47 @@ def test_head_and_accept_rejects():
          sv.SV_ERR_SHAPE)
 
 
+def _chunking(rows, cols, balance=True, grid=256, max_s=8):
+    """K chunks of a phase: S = ceil(steps / 20) for every tile; a balanced
+    phase (not a head) with at least one round of `grid` tile-chunks and a
+    partial last round cuts the last ceil(R / S) tiles (R = the remainder of
+    tile-chunks over whole rounds) into S1 = f S chunks, f = the largest
+    factor that keeps those tiles within one round, chunks of at least one
+    step and at most 8 chunks.  Returns (S, S1, tiles cut into S)."""
+    steps = -(-cols // 256)
+    S = -(-steps // 20)
+    T = -(-rows // 32)
+    if balance and T * S >= grid and (T * S) % grid:
+        tr = -(-((T * S) % grid) // S)
+        f = min(grid // (tr * S), max_s // S, steps // S)
+        if f >= 2:
+            return S, S * f, T - tr
+    return S, S, T
+
+
 def test_workspace_sizes():
-    """K is cut into ceil(steps / 20) chunks of 256-element steps; partial sums
-    (after a fixed 256 KiB counter region) are needed when K is split, or
-    when two matrices may be paired at M > 8 (then each matrix of a pair is a
-    unit of its own and the tile's last unit forms the product; at M <= 8 a
-    unit covers both), and nothing otherwise."""
+    """Partial sums (after a fixed 256 KiB counter region, [n_w][S1][M][rows]
+    fp32) are needed when some tile's K is split over units, or when two
+    matrices may be paired at M > 8 (then each matrix of a pair is a unit of
+    its own and the tile's last unit forms the product; at M <= 8 a unit
+    covers both), and nothing otherwise.  A head keeps one chunking for all
+    tiles."""
     L = sv.lib()
-    for rows, cols, qt, n_w, M, S in [(2560, 2560, 12, 3, 5, 1), (2560, 9728, 14, 1, 5, 2), (9728, 2560, 12, 2, 16, 1),
-                                      (5120, 17408, 14, 1, 5, 4), (17408, 5120, 12, 1, 8, 1),
-                                      (2560, 2560, 14, 2, 5, 1), (17408, 5120, 12, 2, 5, 1), (4096, 10240, 14, 1, 3, 2)]:
-        steps = -(-cols // 256)
-        assert -(-steps // 20) == S
+    cases = [(2560, 2560, 12, 3, 5, (1, 1)), (2560, 9728, 14, 1, 5, (2, 2)), (9728, 2560, 12, 2, 16, (1, 5)),
+             (5120, 17408, 14, 1, 5, (4, 8)), (17408, 5120, 12, 1, 8, (1, 8)), (2560, 2560, 14, 2, 5, (1, 1)),
+             (17408, 5120, 12, 2, 5, (1, 8)), (4096, 10240, 14, 1, 3, (2, 2)), (8192, 5120, 12, 1, 5, (1, 1)),
+             (8192 + 32, 2048, 8, 1, 2, (1, 8)), (2048, 1024, 8, 1, 1, (1, 1))]
+    for rows, cols, qt, n_w, M, (S, S1) in cases:
+        assert _chunking(rows, cols)[:2] == (S, S1), (rows, cols)
         W = (sv.Weight * n_w)(*([_w(qt=qt, rows=rows, cols=cols)] * n_w))
         need = L.sv_matvec_workspace_bytes(W, n_w, ctypes.byref(_act(M=M, K=cols)))
-        if S == 1 and (n_w != 2 or M <= 8):
-            assert need == 0
+        if S1 == 1 and (n_w != 2 or M <= 8):
+            assert need == 0, (rows, cols)
         else:
-            assert need == 256 * 1024 + n_w * S * M * rows * 4
+            assert need == 256 * 1024 + n_w * S1 * M * rows * 4, (rows, cols)
+    # a head is never rebalanced: 17408 rows of K = 5120 stay in one chunk
+    H = _w(qt=12, rows=17408, cols=5120)
+    assert L.sv_head_workspace_bytes(ctypes.byref(H), ctypes.byref(_act(M=5, K=5120)), 0) == 0
 
 
 def _phase(W, A, ep=None, argmax=None):
