@@ -271,11 +271,11 @@ class Pass:
         return g.value
 
     def read_trace(self, n_phases):
-        """[grid, n_phases, 12] uint64 record of the last traced run."""
+        """[grid, n_phases, 16] uint64 record of the last traced run."""
         import numpy as np
         g = ctypes.c_int32()
         _check(lib().sv_pass_trace(self._h, 1, None, 0, ctypes.byref(g)))
-        buf = np.zeros((g.value, n_phases, 12), np.uint64)
+        buf = np.zeros((g.value, n_phases, 16), np.uint64)
         _check(lib().sv_pass_trace(self._h, 1, buf.ctypes.data_as(ctypes.c_void_p), buf.nbytes, None))
         return buf
 

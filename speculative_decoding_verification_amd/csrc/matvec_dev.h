@@ -897,13 +897,17 @@ __device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target,
 }
 
 // Copies n bytes (a multiple of 4) from global memory to LDS with the
-// loads' LDS transfer: 16 bytes per lane when the source and the size allow
-// it, else 4.  Lane l of an instruction writes dst + 16 l (or 4 l), so the
-// LDS destination of each instruction is uniform.
+// loads' LDS transfer: 16 bytes per lane when the source, the destination
+// and the size allow it, else 4.  Lane l of an instruction writes dst + 16 l
+// (or 4 l), so the LDS destination of each instruction is uniform.  The
+// loops stay rolled: this code runs once per staged chunk, after a wait, so
+// its length (instruction-cache misses), not its loop overhead, is what
+// costs.
 __device__ __forceinline__ void dma_copy(uint8_t *dst, const uint8_t *src, int n) {
     const int lane = threadIdx.x & 63;
     if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | static_cast<uintptr_t>(n)) & 15) == 0) {
         const int n16 = n >> 4;
+#pragma unroll 1
         for (int k = 0; 64 * k < n16; k++) {
             const int i = 64 * k + lane;
             if (i < n16)
@@ -912,6 +916,7 @@ __device__ __forceinline__ void dma_copy(uint8_t *dst, const uint8_t *src, int n
         }
     } else {
         const int n4 = n >> 2;
+#pragma unroll 1
         for (int k = 0; 64 * k < n4; k++) {
             const int i = 64 * k + lane;
             if (i < n4)
@@ -927,31 +932,32 @@ __device__ __forceinline__ void dma_copy(uint8_t *dst, const uint8_t *src, int n
 // ... in order, then wave_sum (a fixed order that depends only on the
 // number of partials).
 template <int M, class PD>
-__device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *act, Shared<M> &sh) {
+__device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *act, Shared<M> &sh,
+                                      unsigned long long *tr) {
     const int lane = threadIdx.x & 63;
     const int K = P.K, nsub = K >> 5, cs = g.cs;
-    const int8_t *aq = P.aq;
-    const float *ad = P.ad;
-    const int32_t *as16 = P.as16;
     const float *parts = P.in_parts;
     const int n_parts = P.n_parts;
-    uint8_t *qd = act;
-    float *dd = reinterpret_cast<float *>(act + M * cs * 32);
-    int32_t *xd = reinterpret_cast<int32_t *>(act + M * cs * 36);
     float *pd = reinterpret_cast<float *>(act + M * cs * 44);
-#pragma unroll
-    for (int m = 0; m < M; m++) {
-        dma_copy(qd + m * cs * 32,
-                 reinterpret_cast<const uint8_t *>(aq) + static_cast<int64_t>(m) * K + static_cast<int64_t>(g.s_begin) * 32,
-                 cs * 32);
-        dma_copy(reinterpret_cast<uint8_t *>(dd + m * cs),
-                 reinterpret_cast<const uint8_t *>(ad + static_cast<int64_t>(m) * nsub + g.s_begin), cs * 4);
-        dma_copy(reinterpret_cast<uint8_t *>(xd + m * 2 * cs),
-                 reinterpret_cast<const uint8_t *>(as16 + static_cast<int64_t>(m) * (K >> 4) + 2 * g.s_begin), cs * 8);
+    // three fields, each M rows: codes (row stride K), scales (nsub floats),
+    // code sums (K / 16 ints); the LDS rows are contiguous, field after field
+#pragma unroll 1
+    for (int f = 0; f < 3; f++) {
+        const uint8_t *src = f == 0 ? reinterpret_cast<const uint8_t *>(P.aq) + static_cast<int64_t>(g.s_begin) * 32
+                             : f == 1 ? reinterpret_cast<const uint8_t *>(P.ad + g.s_begin)
+                                      : reinterpret_cast<const uint8_t *>(P.as16 + 2 * g.s_begin);
+        const int64_t sstride = f == 0 ? K : (f == 1 ? nsub * 4 : (K >> 4) * 4);
+        const int row = f == 0 ? cs * 32 : (f == 1 ? cs * 4 : cs * 8);
+        uint8_t *dst = act + (f == 0 ? 0 : (f == 1 ? M * cs * 32 : M * cs * 36));
+#pragma unroll 1
+        for (int m = 0; m < M; m++) dma_copy(dst + m * row, src + m * sstride, row);
     }
     if (parts) dma_copy(reinterpret_cast<uint8_t *>(pd), reinterpret_cast<const uint8_t *>(parts), M * n_parts * 4);
+    if (tr && lane == 0) tr[12] = now();
     // the transfers have written LDS once this wave's loads are complete
     __builtin_amdgcn_s_waitcnt(0);
+    if (tr && lane == 0) tr[13] = now();
+#pragma unroll 1
     for (int m = 0; m < M; m++) {
         float r = 1.0f;
         if (parts) {
@@ -1264,7 +1270,7 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
                     if (lane == 0) sh.abort = 1u;
                 } else {
                     if (tr && lane == 0) tr[1] = now();
-                    stage<M>(P, g, act, sh);
+                    stage<M>(P, g, act, sh, tr);
                     if (tr && lane == 0) tr[2] = now();
                     st_q = aq;
                     st_parts = parts;

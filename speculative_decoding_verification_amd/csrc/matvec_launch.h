@@ -43,8 +43,9 @@ constexpr int kPhaseCounters = kSlots * kReplicas;   // counter lines per phase
 // input ready, input staged, first unit computed, first unit done, last
 // unit done; units run; the first unit's finish: entry, outputs written,
 // partial sums drained (split tiles); HW_ID | XCC_ID << 32; the first
-// unit's hand-off drained.
-constexpr int kTraceWords = 12;
+// unit's hand-off drained; the first staging's transfers issued, and
+// landed; two unused.
+constexpr int kTraceWords = 16;
 
 // Division by a divisor d >= 1 fixed per phase: n / d = (n * m) >> sh for
 // every n < 2^31, with l = ceil(log2 d), m = ceil(2^(31 + l) / d) and
