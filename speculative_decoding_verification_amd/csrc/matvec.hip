@@ -23,7 +23,7 @@
 namespace sv {
 
 // ------------------------------------------------------------- dispatch
-using PassFn = void (*)(int, size_t, hipStream_t, const PhaseDesc *, int, unsigned *, int, ArgmaxList,
+using PassFn = void (*)(int, size_t, hipStream_t, const PhaseDesc *, int, const uint32_t *, unsigned *, int, ArgmaxList,
                         unsigned long long *);
 using PhaseFn = void (*)(int, size_t, hipStream_t, const PhaseDesc &, int);
 using OccFn = int (*)(size_t);
@@ -359,6 +359,7 @@ struct sv_pass {
     int M, n_phases, grid, CS, NP;
     size_t lds;
     sv::PhaseDesc *table;        // device
+    uint32_t *sched;             // device: per-workgroup unit lists (see schedule)
     unsigned *ctl;               // device: control words, completion slots
     unsigned long long *trace;   // device: [kMaxGrid][n_phases][kTraceWords]
     sv::ArgmaxList am;
@@ -368,12 +369,12 @@ struct sv_pass {
 
 namespace sv {
 
-// Workspace of a pass, in order: phase table | control words and
-// completion counters | trace | per phase with split tiles: its tile
+// Workspace of a pass, in order: phase table | schedule | control words
+// and completion counters | trace | per phase with split tiles: its tile
 // counters, then its partial sums.  Every phase has scratch of its own, so
 // phases that run side by side never share counters or partials.
 struct PassLayout {
-    size_t table, ctl, trace, scratch, total;
+    size_t table, sched, ctl, trace, scratch, total;
     std::vector<size_t> tiles_off, part_off;   // per phase, from the start of the scratch
 };
 
@@ -398,12 +399,120 @@ static int plan_pass(const sv_phase *phases, int32_t n_phases, std::vector<Phase
             scratch += round256(partial_bytes(host[i], ph.A.M));
         }
     }
+    size_t units = 0;
+    for (const PhaseDesc &P : host) {
+        SV_REQUIRE(P.n_units < (1 << 20), SV_ERR_SHAPE, "pass: a phase has more than 2^20 units");
+        units += static_cast<size_t>(P.n_units);
+    }
+    SV_REQUIRE(n_phases < (1 << 12), SV_ERR_ARG, "pass: at most 4095 phases");
     L.table = round256(static_cast<size_t>(n_phases) * sizeof(PhaseDesc));
+    L.sched = round256((static_cast<size_t>(kMaxGrid) + 1 + units) * 4);
     L.ctl = round256(static_cast<size_t>(kSlotStride) * (1 + n_phases * kPhaseCounters) * 4);
     L.trace = round256(static_cast<size_t>(kMaxGrid) * n_phases * kTraceWords * 8);
     L.scratch = scratch;
-    L.total = L.table + L.ctl + L.trace + L.scratch;
+    L.total = L.table + L.sched + L.ctl + L.trace + L.scratch;
     return SV_OK;
+}
+
+// The unit geometry of the device's unit_pos, for the host's schedule.
+static void host_unit_range(const PhaseDesc &P, uint32_t u, int &c0, int &c1, int &s_begin, int &cs) {
+    const int per_tile = P.per_tile, S = P.S, head = P.T1 * per_tile;
+    int chunk, nch;
+    if (static_cast<int>(u) < head) {
+        chunk = (static_cast<int>(u) % per_tile) % S;
+        nch = S;
+    } else {
+        const int v = static_cast<int>(u) - head, f = P.S1 / S;
+        const int rem = v % per_tile, q = v / per_tile;
+        chunk = f * (rem % S) + q % f;
+        nch = P.S1;
+    }
+    c0 = chunk * P.steps / nch;
+    c1 = (chunk + 1) * P.steps / nch;
+    s_begin = c0 * 8;
+    cs = std::min((c1 - c0) * 8, P.K / 32 - s_begin);
+}
+
+// The order in which each workgroup of a pass runs units: the host
+// simulates the launch with a plain cost model (a unit costs its weight
+// bytes at one workgroup's streaming rate; a phase whose input another
+// phase writes starts a hand-off after that phase's last unit; staging an
+// input chunk costs a fixed time that grows with M) and gives every unit,
+// phase by phase in unit order, to the workgroup that can start it first,
+// preferring one that has its input chunk staged already.  So a phase that
+// no later phase waits for fills the workgroups a narrower phase leaves
+// idle, instead of delaying the phase after it.  Each workgroup's list is
+// in phase order and every wait is for an earlier phase, so the launch
+// cannot deadlock whatever the model gets wrong; the model only decides
+// how well the work is spread.
+static void schedule(const std::vector<PhaseDesc> &host, const std::vector<int> &producer, int M, int G,
+                     std::vector<uint32_t> &out) {
+    const int n = static_cast<int>(host.size());
+    const double rate = 26000.0 / (1.0 + 0.09 * (M - 1));   // bytes per microsecond per workgroup
+    const double unit_ovh = 0.5, hand = 1.0, stage = 1.4 + 0.8 * (M - 1);
+    std::vector<double> free_at(G, 0.0), phase_end(n, 0.0);
+    std::vector<const void *> st_in(G, nullptr);
+    std::vector<int> st_b(G, -1), st_c(G, 0);
+    std::vector<std::vector<uint32_t>> lists(G);
+    for (int p = 0; p < n; p++) {
+        const PhaseDesc &P = host[p];
+        const double ready = producer[p] >= 0 ? phase_end[producer[p]] + hand : 0.0;
+        const double row_bytes = static_cast<double>(P.bbytes) / 16.0 * (P.fused ? 2.0 : 1.0);
+        for (uint32_t u = 0; u < static_cast<uint32_t>(P.n_units); u++) {
+            int c0, c1, sb, cs;
+            host_unit_range(P, u, c0, c1, sb, cs);
+            const double cost = kRows * (c1 - c0) * row_bytes / rate + unit_ovh;
+            int best = 0;
+            double best_t = 1e300;
+            bool best_staged = false;
+            for (int w = 0; w < G; w++) {
+                const bool staged = st_in[w] == P.aq && sb >= st_b[w] && sb + cs <= st_b[w] + st_c[w];
+                const double t0 = std::max(free_at[w], ready) + (staged ? 0.0 : stage);
+                if (t0 < best_t - 1e-9) {
+                    best_t = t0;
+                    best = w;
+                    best_staged = staged;
+                }
+            }
+            if (!best_staged) {
+                st_in[best] = P.aq;
+                st_b[best] = sb;
+                st_c[best] = cs;
+            }
+            free_at[best] = best_t + cost;
+            phase_end[p] = std::max(phase_end[p], free_at[best]);
+            lists[best].push_back(static_cast<uint32_t>(p) << 20 | u);
+        }
+    }
+    out.assign(static_cast<size_t>(G) + 1, 0u);
+    for (int w = 0; w < G; w++) out[w + 1] = out[w] + static_cast<uint32_t>(lists[w].size());
+    for (int w = 0; w < G; w++) out.insert(out.end(), lists[w].begin(), lists[w].end());
+}
+
+// Every (phase, unit) exactly once, each list in phase order: what the
+// kernel relies on for in-range units and for waits that always end.
+static bool schedule_ok(const std::vector<PhaseDesc> &host, int G, const std::vector<uint32_t> &s) {
+    if (s.size() < static_cast<size_t>(G) + 1) return false;
+    size_t total = 0;
+    std::vector<size_t> base(host.size() + 1, 0);
+    for (size_t p = 0; p < host.size(); p++) base[p + 1] = base[p] + static_cast<size_t>(host[p].n_units);
+    total = base.back();
+    if (s[G] != total || s.size() != static_cast<size_t>(G) + 1 + total) return false;
+    std::vector<uint8_t> seen(total, 0);
+    for (int w = 0; w < G; w++) {
+        if (s[w] > s[w + 1]) return false;
+        int prev = -1;
+        for (uint32_t i = s[w]; i < s[w + 1]; i++) {
+            const uint32_t e = s[G + 1 + i];
+            const int p = static_cast<int>(e >> 20);
+            const uint32_t u = e & 0xFFFFFu;
+            if (p >= static_cast<int>(host.size()) || p < prev || u >= static_cast<uint32_t>(host[p].n_units))
+                return false;
+            if (seen[base[p] + u]++) return false;
+            prev = p;
+        }
+    }
+    return true;
 }
 
 struct Span {
@@ -508,13 +617,13 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
     rc = link_phases(host, M, producer);
     if (rc) return rc;
     uint8_t *b = static_cast<uint8_t *>(workspace);
-    unsigned *ctl = reinterpret_cast<unsigned *>(b + L.table);
-    uint8_t *scratch = b + L.table + L.ctl + L.trace;
+    uint32_t *sched = reinterpret_cast<uint32_t *>(b + L.table);
+    unsigned *ctl = reinterpret_cast<unsigned *>(b + L.table + L.sched);
+    uint8_t *scratch = b + L.table + L.sched + L.ctl + L.trace;
     ArgmaxList am{};
     std::vector<int> readers(n_phases, 0);
     for (int i = 0; i < n_phases; i++)
         if (producer[i] >= 0) readers[producer[i]]++;
-    uint32_t tickets = 0;
     for (int i = 0; i < n_phases; i++) {
         PhaseDesc &P = host[i];
         if (needs_partials(P)) {
@@ -526,12 +635,6 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
         // ep_src alone.
         P.count_all = (P.S1 > 1 || P.ep_mode != SV_EP_QUANT) ? 1 : 0;
         P.ready = readers[i] ? ctl + kSlotStride * (1 + i * kPhaseCounters) : nullptr;
-        // a phase whose last round is cut finer starts on workgroup 0 of a
-        // round, so the finer chunk each workgroup gets lies inside the
-        // chunk it staged for its earlier units of the phase
-        if (P.T1 < P.n_tiles) tickets = (tickets + kBalanceGrid - 1) / kBalanceGrid * kBalanceGrid;
-        P.unit_base = tickets;
-        tickets += static_cast<uint32_t>(P.n_units);
         if (P.argmax) {
             SV_REQUIRE(am.n < kMaxArgmax, SV_ERR_ARG, "pass_create: at most 4 phases may have an argmax");
             am.p[am.n] = P.argmax;
@@ -574,15 +677,24 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
     p->NP = np;
     p->lds = lds;
     p->table = reinterpret_cast<PhaseDesc *>(b);
+    p->sched = sched;
     p->ctl = ctl;
-    p->trace = reinterpret_cast<unsigned long long *>(b + L.table + L.ctl);
+    p->trace = reinterpret_cast<unsigned long long *>(b + L.table + L.sched + L.ctl);
     p->tracing = false;
     p->am = am;
     p->host = std::move(host);
     p->grid = std::min(prop.multiProcessorCount * std::min(occ, 2), kMaxGrid);
+    std::vector<uint32_t> plan;
+    schedule(p->host, producer, M, p->grid, plan);
+    if (!schedule_ok(p->host, p->grid, plan)) {
+        delete p;
+        return fail(SV_ERR_ARG, "pass_create: internal error: inconsistent schedule");
+    }
     rc = hip_check(hipMemcpy(p->table, p->host.data(), static_cast<size_t>(n_phases) * sizeof(PhaseDesc),
                              hipMemcpyHostToDevice),
                    "pass_create upload");
+    if (!rc)
+        rc = hip_check(hipMemcpy(sched, plan.data(), plan.size() * 4, hipMemcpyHostToDevice), "pass_create schedule");
     if (!rc) rc = hip_check(hipMemset(p->ctl, 0, L.ctl), "pass_create ctl");
     if (!rc) rc = hip_check(hipMemset(p->trace, 0, L.trace), "pass_create trace");
     if (!rc && L.scratch) rc = hip_check(hipMemset(scratch, 0, L.scratch), "pass_create scratch");
@@ -599,7 +711,7 @@ extern "C" int sv_pass_run(const sv_pass *p, void *stream) {
     using namespace sv;
     SV_REQUIRE(p, SV_ERR_ARG, "pass_run: NULL pass");
     hipStream_t st = as_stream(stream);
-    kPassFns[p->M - 1](p->grid, p->lds, st, p->table, p->n_phases, p->ctl, p->CS, p->am,
+    kPassFns[p->M - 1](p->grid, p->lds, st, p->table, p->n_phases, p->sched, p->ctl, p->CS, p->am,
                        p->tracing ? p->trace : nullptr);
     return hip_check(hipGetLastError(), "pass_run launch");
 }

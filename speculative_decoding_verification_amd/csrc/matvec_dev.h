@@ -69,42 +69,58 @@ struct RingDepth {
 // ------------------------------------------------------------ tables
 // Phase descriptors are read with scalar loads: from the pass's table in
 // device memory through a constant-address-space pointer, or from the
-// kernel argument of a single call.
+// kernel argument of a single call.  A cursor walks the units a workgroup
+// runs: in a pass the host's schedule lists them, per workgroup and in
+// phase order (entry = phase << 20 | unit); in a single call workgroup b
+// runs unit b.
+struct UnitCur {
+    int p;
+    uint32_t u;
+    uint32_t i, end;   // the workgroup's schedule entries [i, end) (pass)
+};
+
 struct ManyTab {
     const SV_AS4 PhaseDesc *t;
+    const SV_AS4 uint32_t *sched;   // [G + 1] entry offsets per workgroup, then the entries
+    int n;
+    uint32_t G;
     __device__ __forceinline__ const SV_AS4 PhaseDesc &operator[](int p) const { return t[p]; }
+    __device__ __forceinline__ void decode(UnitCur &c) const {
+        if (c.i < c.end) {
+            const uint32_t e = sched[G + 1 + c.i];
+            c.p = static_cast<int>(e >> 20);
+            c.u = e & 0xFFFFFu;
+        } else {
+            c.p = n;
+        }
+    }
+    __device__ __forceinline__ void first(uint32_t b, UnitCur &c) const {
+        c.i = sched[b];
+        c.end = sched[b + 1];
+        decode(c);
+    }
+    __device__ __forceinline__ void next(UnitCur &c) const {
+        c.i++;
+        decode(c);
+    }
 };
 struct OneTab {
     PhaseDesc P;
     __device__ __forceinline__ const PhaseDesc &operator[](int) const { return P; }
-};
-
-// The units of phase p that workgroup b of G runs: u0, u0 + G, ... < n_units.
-struct UnitCur {
-    int p;
-    uint32_t u;
-};
-
-template <class Tab>
-__device__ __forceinline__ void unit_seek(const Tab &tab, int n_phases, uint32_t b, uint32_t G, UnitCur &c) {
-    for (; c.p < n_phases; c.p++) {
-        const uint32_t base = static_cast<uint32_t>(tab[c.p].unit_base);
-        c.u = (b + G - base % G) % G;
-        if (c.u < static_cast<uint32_t>(tab[c.p].n_units)) return;
+    __device__ __forceinline__ void first(uint32_t b, UnitCur &c) const {
+        c.u = b;
+        c.p = b < static_cast<uint32_t>(P.n_units) ? 0 : 1;
     }
+    __device__ __forceinline__ void next(UnitCur &c) const { c.p = 1; }   // one unit per workgroup
+};
+
+template <class Tab>
+__device__ __forceinline__ void unit_first(const Tab &tab, int, uint32_t b, uint32_t, UnitCur &c) {
+    tab.first(b, c);
 }
 template <class Tab>
-__device__ __forceinline__ void unit_first(const Tab &tab, int n_phases, uint32_t b, uint32_t G, UnitCur &c) {
-    c.p = 0;
-    c.u = 0;
-    unit_seek(tab, n_phases, b, G, c);
-}
-template <class Tab>
-__device__ __forceinline__ void unit_next(const Tab &tab, int n_phases, uint32_t b, uint32_t G, UnitCur &c) {
-    c.u += G;
-    if (c.u < static_cast<uint32_t>(tab[c.p].n_units)) return;
-    c.p++;
-    unit_seek(tab, n_phases, b, G, c);
+__device__ __forceinline__ void unit_next(const Tab &tab, int, uint32_t, uint32_t, UnitCur &c) {
+    tab.next(c);
 }
 
 // Geometry of a unit: tile, K chunk (of the tile's nch) and matrix; the
@@ -1330,8 +1346,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
 // launch.
 template <int M>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void pass_kernel(const PhaseDesc *__restrict__ table, int n_phases,
-                                                        unsigned *ctl, int CS, ArgmaxList am,
-                                                        unsigned long long *trace) {
+                                                        const uint32_t *__restrict__ sched, unsigned *ctl, int CS,
+                                                        ArgmaxList am, unsigned long long *trace) {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ Shared<M> sh;
     __shared__ int last;
@@ -1349,7 +1365,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         if (threadIdx.x == 0) st_dev(ctl + kCtlArgmaxClear, 1u);
     }
     __syncthreads();
-    const ManyTab tab{reinterpret_cast<const SV_AS4 PhaseDesc *>(reinterpret_cast<uintptr_t>(table))};
+    const ManyTab tab{reinterpret_cast<const SV_AS4 PhaseDesc *>(reinterpret_cast<uintptr_t>(table)),
+                      reinterpret_cast<const SV_AS4 uint32_t *>(reinterpret_cast<uintptr_t>(sched)), n_phases,
+                      gridDim.x};
     if (threadIdx.x < kCompWaves * 64) compute_waves<M>(tab, n_phases, blockIdx.x, gridDim.x, smem, sh);
     else control_wave<M>(tab, n_phases, blockIdx.x, gridDim.x, smem, sh, status, cleared, trace);
     __syncthreads();

@@ -13,9 +13,10 @@ namespace sv {
 
 template <>
 void launch_pass_m<SV_INST_M>(int grid, size_t lds, hipStream_t st, const PhaseDesc *table, int n_phases,
-                              unsigned *ctl, int CS, ArgmaxList am, unsigned long long *trace) {
-    hipLaunchKernelGGL((pass_kernel<SV_INST_M>), dim3(grid), dim3(kThreads), lds, st, table, n_phases, ctl, CS, am,
-                       trace);
+                              const uint32_t *sched, unsigned *ctl, int CS, ArgmaxList am,
+                              unsigned long long *trace) {
+    hipLaunchKernelGGL((pass_kernel<SV_INST_M>), dim3(grid), dim3(kThreads), lds, st, table, n_phases, sched, ctl, CS,
+                       am, trace);
 }
 
 template <>

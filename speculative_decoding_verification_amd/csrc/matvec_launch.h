@@ -90,7 +90,6 @@ struct PhaseDesc {
     unsigned *ready;          // finished units of this phase (persistent mode; NULL: no reader)
     const unsigned *wait;     // finished units of the input's producer (NULL: input written before)
     uint32_t wait_target;
-    uint32_t unit_base;       // units of all earlier phases (persistent mode)
 };
 
 // The argmax buffers a pass clears before any head workgroup adds to them.
@@ -102,8 +101,8 @@ struct ArgmaxList {
 
 // Defined once per M in matvec_inst.hip.
 template <int M>
-void launch_pass_m(int grid, size_t lds, hipStream_t st, const PhaseDesc *table, int n_phases, unsigned *ctl, int CS,
-                   ArgmaxList am, unsigned long long *trace);
+void launch_pass_m(int grid, size_t lds, hipStream_t st, const PhaseDesc *table, int n_phases, const uint32_t *sched,
+                   unsigned *ctl, int CS, ArgmaxList am, unsigned long long *trace);
 template <int M>
 void launch_phase_m(int grid, size_t lds, hipStream_t st, const PhaseDesc &P, int CS);
 template <int M>
