@@ -63,7 +63,11 @@ constexpr int kStepParts = kCompWaves / 2;   // compute waves per half tile
 // no result.
 template <int M>
 struct RingDepth {
-    static constexpr int value = M <= 2 ? 4 : (M <= 5 ? 3 : 2);
+#ifdef SV_RING
+    static constexpr int value = SV_RING;
+#else
+    static constexpr int value = M == 1 ? 5 : (M <= 2 ? 4 : (M <= 5 ? 3 : 2));
+#endif
 };
 
 // ------------------------------------------------------------ tables
@@ -871,16 +875,20 @@ __device__ __forceinline__ void compute_waves(const Tab &tab, int n_phases, uint
         for (int m = 0; m < M; m++) st.accu[p][m] = 0.0f;
     // separate slots (no array): every access has a constant address from
     // the start, so the slots live in registers
-    Slot s0, s1, s2, s3;
+    Slot s0, s1, s2, s3, s4, s5;
     prime<M>(tab, n_phases, b, G, wave, st, s0);
     prime<M>(tab, n_phases, b, G, wave, st, s1);
     if constexpr (D > 2) prime<M>(tab, n_phases, b, G, wave, st, s2);
     if constexpr (D > 3) prime<M>(tab, n_phases, b, G, wave, st, s3);
+    if constexpr (D > 4) prime<M>(tab, n_phases, b, G, wave, st, s4);
+    if constexpr (D > 5) prime<M>(tab, n_phases, b, G, wave, st, s5);
     while (st.go) {
         ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s0);
         ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s1);
         if constexpr (D > 2) ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s2);
         if constexpr (D > 3) ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s3);
+        if constexpr (D > 4) ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s4);
+        if constexpr (D > 5) ring_step<M>(tab, n_phases, b, G, wave, smem, sh, st, s5);
     }
     __builtin_amdgcn_s_waitcnt(0);
 }
@@ -944,9 +952,7 @@ __device__ __forceinline__ void dma_copy(uint8_t *dst, const uint8_t *src, int n
 
 // Copies the input chunk of a phase (codes, scales, code sums and, if the
 // input is RMS-normalised, its partials) into LDS with load-to-LDS
-// transfers, then forms the RMS factors: lane l adds partials l, l + 64,
-// ... in order, then wave_sum (a fixed order that depends only on the
-// number of partials).
+// transfers and waits for them to land.
 template <int M, class PD>
 __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *act, Shared<M> &sh,
                                       unsigned long long *tr) {
@@ -973,6 +979,18 @@ __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *ac
     // the transfers have written LDS once this wave's loads are complete
     __builtin_amdgcn_s_waitcnt(0);
     if (tr && lane == 0) tr[13] = now();
+}
+
+// The RMS factors of the staged input (only the control wave reads them, in
+// the unit's finish, so they are formed after the compute waves are let go):
+// lane l adds partials l, l + 64, ... in order, then wave_sum (a fixed order
+// that depends only on the number of partials).
+template <int M, class PD>
+__device__ __forceinline__ void stage_rscale(const PD &P, const UnitPos &g, const uint8_t *act, Shared<M> &sh) {
+    const int lane = threadIdx.x & 63;
+    const int K = P.K, n_parts = P.n_parts;
+    const float *pd = reinterpret_cast<const float *>(act + M * g.cs * 44);
+    const bool parts = P.in_parts != nullptr;
 #pragma unroll 1
     for (int m = 0; m < M; m++) {
         float r = 1.0f;
@@ -1280,6 +1298,7 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
                             (static_cast<unsigned long long>(__builtin_amdgcn_s_getreg(0xF814)) << 32);
                 }
             }
+            bool fresh = false;
             if (!inside) {
                 const unsigned *wt = P.wait;
                 if (wt && !wait_ready(wt, P.wait_target, status)) {
@@ -1292,6 +1311,7 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
                     st_parts = parts;
                     st_begin = g.s_begin;
                     st_cs = g.cs;
+                    fresh = true;
                 }
             }
             if (lane == 0) {
@@ -1300,6 +1320,7 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
             }
             lds_barrier();   // B1
             if (sh.abort) break;
+            if (fresh) stage_rscale<M>(P, g, act, sh);
         }
         const float g_cur = gamma_of(P, c.u);   // in flight while the unit computes
         lds_barrier();       // B2: the compute waves have written the unit's partial sums
