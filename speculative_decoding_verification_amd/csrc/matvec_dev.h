@@ -174,7 +174,7 @@ __device__ __forceinline__ UnitPos unit_pos(const PD &P, uint32_t u) {
 // make (at least one: a wave with no step still passes through the unit).
 // A Q4_K record of one matrix is 5 words, so its items carry two steps.
 struct WaveSpan {
-    int w0, w1, sp, nitems;
+    int w0, w1, sp, nh, nitems;   // nh items per matrix
 };
 template <class PD>
 __device__ __forceinline__ WaveSpan wave_span(const PD &P, const UnitPos &g, int wave) {
@@ -183,8 +183,10 @@ __device__ __forceinline__ WaveSpan wave_span(const PD &P, const UnitPos &g, int
     s.w0 = g.c0 + part * tc / kStepParts;
     s.w1 = g.c0 + (part + 1) * tc / kStepParts;
     s.sp = P.qtype == SV_Q4_K ? 2 : 1;
-    // a fused pair alternates gate and up items over the same steps
-    s.nitems = max(1, (s.w1 - s.w0 + s.sp - 1) >> (s.sp - 1)) * (P.fused ? 2 : 1);
+    // a fused pair runs the gate items, then the up items, over the same
+    // steps (one set of accumulators serves both in turn)
+    s.nh = max(1, (s.w1 - s.w0 + s.sp - 1) >> (s.sp - 1));
+    s.nitems = s.nh * (P.fused ? 2 : 1);
     return s;
 }
 
@@ -524,7 +526,6 @@ struct ItemCur {
     const uint8_t *wm;   // matrix of the current unit
     int qtype, fused, K, N, wrows;
     uint32_t bbytes;   // bytes of a weight block
-    uint32_t fsh;      // 1 for a fused pair (items alternate matrices), else 0
     uint32_t sp;       // steps per item (2 for Q4_K)
     uint32_t last;     // the last step an item of this wave may read
     const int32_t *row_ids;
@@ -548,7 +549,6 @@ __device__ __forceinline__ void cur_phase(const Tab &tab, ItemCur &c) {
     c.N = P.N;
     c.wrows = P.wrows;
     c.bbytes = P.bbytes;
-    c.fsh = static_cast<uint32_t>(P.fused);
     c.sp = P.qtype == SV_Q4_K ? 2u : 1u;
     c.row_ids = P.row_ids;
 }
@@ -714,10 +714,10 @@ __device__ __forceinline__ uint32_t w4(const uint8_t *p) { return gld(reinterpre
 
 __device__ __forceinline__ void load_item(Slot &s, const ItemCur &c) {
     // integer arithmetic on wave-uniform fields only (no booleans), so the
-    // block addresses stay in scalar registers: a fused pair's item 2k is
-    // gate, 2k + 1 up, over the same steps
-    const uint32_t item = static_cast<uint32_t>(c.item);
-    const uint32_t it = item >> c.fsh, odd = item & c.fsh;
+    // block addresses stay in scalar registers: a fused pair's items
+    // [0, nh) are gate, [nh, 2 nh) up, over the same steps
+    const uint32_t item = static_cast<uint32_t>(c.item), nh = static_cast<uint32_t>(c.s.nh);
+    const uint32_t odd = item >= nh ? 1u : 0u, it = item - odd * nh;
     const uint32_t t0 = min(static_cast<uint32_t>(c.s.w0) + it * c.sp, c.last);
     const uint32_t t1 = min(t0 + c.sp - 1u, c.last);
     const uint64_t wm = reinterpret_cast<uint64_t>(c.wm), w1 = reinterpret_cast<uint64_t>(c.w1);
@@ -740,16 +740,24 @@ template <int QT, int I0, int M>
 __device__ __forceinline__ void step_terms(const Slot &s, const ActLds &A, int sl, float (&acc)[2][M],
                                            uint32_t hs0, uint32_t hs1) {
     const int jl = threadIdx.x & 7;
+    // the activation record of position m + 1 is read while position m is
+    // computed, and the first one while the weights are decoded, so the LDS
+    // latency hides behind arithmetic
+    ARec cur;
+    read_act(cur, A, 0, sl);
     WDec d0, d1;
     decode_w<QT>(d0, rec_of<QT, I0>(s, hs0), jl);
     decode_w<QT>(d1, rec_of<QT, I0 + 1>(s, hs1), jl);
 #pragma unroll
     for (int m = 0; m < M; m++) {
-        ARec ar;
-        read_act(ar, A, m, sl);
-        const AExt ae = act_ext(ar);
-        acc[0][m] = block_term<QT>(d0, ar, ae, acc[0][m]);
-        acc[1][m] = block_term<QT>(d1, ar, ae, acc[1][m]);
+        ARec nxt;
+        if (m + 1 < M) read_act(nxt, A, m + 1, sl);
+        // keep the reads above the arithmetic that does not need them
+        __builtin_amdgcn_sched_barrier(0);
+        const AExt ae = act_ext(cur);
+        acc[0][m] = block_term<QT>(d0, cur, ae, acc[0][m]);
+        acc[1][m] = block_term<QT>(d1, cur, ae, acc[1][m]);
+        if (m + 1 < M) cur = nxt;
     }
 }
 
@@ -758,7 +766,7 @@ template <int M>
 __device__ __forceinline__ void consume(const Slot &s, const ItemCur &c, const ActLds &A, float (&acc)[2][M]) {
     const int jl = threadIdx.x & 7;
     const int64_t nsub = c.K >> 5;
-    const int it = c.item >> c.fsh;
+    const int it = c.item - (c.item >= c.s.nh ? c.s.nh : 0);
     if (c.qtype == SV_Q4_K) {
         const int t = c.s.w0 + it * 2;
         if (t < c.s.w1) step_terms<SV_Q4_K, 0, M>(s, A, t * 8 + jl - A.begin, acc, 0u, 0u);
@@ -800,8 +808,7 @@ struct CompState {
     int buf;          // wave-partial buffer of the current unit
     int stb, stc;     // staged sub-blocks [stb, stb + stc) (as the control wave published them)
     ActLds A;
-    float acc[2][M];              // matrix of the unit (gate of a fused pair)
-    float accu[M <= 8 ? 2 : 1][M]; // up of a fused pair (M <= 8 only)
+    float acc[2][M];  // the matrix being computed (gate, then up, of a fused pair)
 };
 
 // One ring step: consume the item in slot s (if the compute cursor is
@@ -825,20 +832,13 @@ __device__ __forceinline__ void ring_step(const Tab &tab, int n_phases, uint32_t
             st.A = act_lds(act_base<M>(smem), M, st.stc, st.stb);
         }
     }
-    if (st.go) {
-        if constexpr (M <= 8) {
-            if (st.C.fused && (st.C.item & 1)) consume<M>(s, st.C, st.A, st.accu);
-            else consume<M>(s, st.C, st.A, st.acc);
-        } else {
-            consume<M>(s, st.C, st.A, st.acc);
-        }
-    }
+    if (st.go) consume<M>(s, st.C, st.A, st.acc);
     load_item(s, st.L);
     if (st.lv) st.lv = cur_advance_keep(tab, n_phases, b, G, st.L, wave, true);
+    // a fused pair's gate sums are written after its last gate item
+    if (st.go && st.C.fused && st.C.item == st.C.s.nh - 1) put_partials<M>(wpart_buf<M>(smem, st.buf), st.acc, 0);
     if (st.go && st.C.item == st.C.s.nitems - 1) {
-        put_partials<M>(wpart_buf<M>(smem, st.buf), st.acc, 0);
-        if constexpr (M <= 8)
-            if (st.C.fused) put_partials<M>(wpart_buf<M>(smem, st.buf), st.accu, 1);
+        put_partials<M>(wpart_buf<M>(smem, st.buf), st.acc, st.C.fused ? 1 : 0);
         lds_barrier();   // B2: the unit's partial sums are written
         st.buf ^= 1;
         if (sh.abort) st.go = false;
@@ -869,10 +869,6 @@ __device__ __forceinline__ void compute_waves(const Tab &tab, int n_phases, uint
     for (int p = 0; p < 2; p++)
 #pragma unroll
         for (int m = 0; m < M; m++) st.acc[p][m] = 0.0f;
-#pragma unroll
-    for (int p = 0; p < (M <= 8 ? 2 : 1); p++)
-#pragma unroll
-        for (int m = 0; m < M; m++) st.accu[p][m] = 0.0f;
     // separate slots (no array): every access has a constant address from
     // the start, so the slots live in registers
     Slot s0, s1, s2, s3, s4, s5;
