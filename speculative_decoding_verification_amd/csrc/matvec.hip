@@ -151,13 +151,36 @@ static void decompose(PhaseDesc &P, bool balance) {
     P.div_S1 = fast_div(static_cast<uint32_t>(P.S1));
 }
 
-// LDS of a workgroup: the compute waves' partial sums (two buffers), then
-// the staged input chunk of all M positions and, for an RMS-normalised
-// input, its partials; the largest phase sets the size.
-static size_t wpart_bytes(int M) { return static_cast<size_t>(2) * 8 * 2 * M * 16 * 4; }
+// LDS of a workgroup: the compute waves' partial sums (two buffers, two
+// matrices each where a unit may cover a fused pair, M <= 8), then the
+// staged input chunk of all M positions and, where P.parts_lds, the RMS
+// partials of the input; the largest phase sets the size.
+static size_t wpart_bytes(int M) { return static_cast<size_t>(2) * 8 * (M <= 8 ? 2 : 1) * M * 16 * 4; }
+
+static size_t parts_bytes(const PhaseDesc &P, int M) {
+    return P.in_parts ? static_cast<size_t>(M) * P.n_parts * 4 : 0;
+}
 
 static size_t phase_lds(const PhaseDesc &P, int M) {
-    return static_cast<size_t>(M) * P.chunk_sub * kActRec + (P.in_parts ? static_cast<size_t>(M) * P.n_parts * 4 : 0);
+    return static_cast<size_t>(M) * P.chunk_sub * kActRec + (P.parts_lds ? parts_bytes(P, M) : 0);
+}
+
+// Stages the RMS partials of every phase into LDS when the launch's LDS
+// still fits the device with them (the factors are then formed from LDS
+// right after the staging wait); otherwise the factors read them from
+// global memory.  The sum is the same either way.
+static int place_parts(PhaseDesc *P, int n, int M) {
+    size_t with = 0;
+    for (int i = 0; i < n; i++)
+        with = std::max(with, static_cast<size_t>(M) * P[i].chunk_sub * kActRec + parts_bytes(P[i], M));
+    with += wpart_bytes(M);
+    size_t limit = kDefaultLds;
+    if (with > kDefaultLds) {
+        const int rc = lds_limit(&limit);
+        if (rc) return rc;
+    }
+    for (int i = 0; i < n; i++) P[i].parts_lds = P[i].in_parts && with <= limit ? 1 : 0;
+    return SV_OK;
 }
 
 static bool needs_partials(const PhaseDesc &P) {
@@ -288,8 +311,10 @@ static int launch_single(PhaseDesc &P, int M, void *ws, size_t ws_bytes, hipStre
         P.partial = reinterpret_cast<float *>(b + kCounterBytes);
     }
     const int CS = P.chunk_sub;
+    int rc = place_parts(&P, 1, M);
+    if (rc) return rc;
     const size_t lds = wpart_bytes(M) + phase_lds(P, M);
-    int rc = prepare_lds(M, lds);
+    rc = prepare_lds(M, lds);
     if (rc) return rc;
     kPhaseFns[M - 1](P.n_units, lds, st, P, CS);
     return hip_check(hipGetLastError(), "projection launch");
@@ -651,6 +676,8 @@ extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *wo
         P.wait = Q.ready;
         P.wait_target = static_cast<uint32_t>(Q.count_all ? Q.n_units : Q.n_tiles);
     }
+    rc = place_parts(host.data(), n_phases, M);
+    if (rc) return rc;
     int chunk = 0, np = 0;
     size_t lds = 0;
     for (auto &P : host) {

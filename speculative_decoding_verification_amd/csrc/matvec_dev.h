@@ -385,7 +385,8 @@ __device__ __forceinline__ float block_term(const WDec &w, const ARec &a, const 
 
 // LDS layout of a staged chunk of cs sub-blocks of all M positions: codes
 // [M][cs][32] (the global bytes as they are), scales [M][cs] fp32, code sums
-// [M][cs][2] int32; the RMS partials of the input follow, [M][n_parts].
+// [M][cs][2] int32; where they are staged, the RMS partials of the input
+// follow, [M][n_parts].
 struct ActLds {
     const uint8_t *q;
     const float *d;
@@ -498,15 +499,20 @@ struct Shared {
     int stb, stc;   // staged sub-blocks [stb, stb + stc), published before B1
 };
 
-// Dynamic LDS: wave partials [2 buffers][8 waves][2 matrices][M][16 rows]
-// fp32, then the staged input chunk and its RMS partials.
+// Dynamic LDS: wave partials [2 buffers][8 waves][NMat][M][16 rows] fp32
+// (two matrices where a unit may cover a fused pair, M <= 8), then the
+// staged input chunk.
+template <int M>
+struct NMat {
+    static constexpr int value = M <= 8 ? 2 : 1;
+};
 template <int M>
 __device__ __forceinline__ float *wpart_buf(uint8_t *smem, int buf) {
-    return reinterpret_cast<float *>(smem) + buf * (kCompWaves * 2 * M * 16);
+    return reinterpret_cast<float *>(smem) + buf * (kCompWaves * NMat<M>::value * M * 16);
 }
 template <int M>
 __device__ __forceinline__ uint8_t *act_base(uint8_t *smem) {
-    return smem + 2 * kCompWaves * 2 * M * 16 * 4;
+    return smem + 2 * kCompWaves * NMat<M>::value * M * 16 * 4;
 }
 
 // Trace record of a (workgroup, phase) (control wave): real-time counter at
@@ -740,9 +746,11 @@ template <int QT, int I0, int M>
 __device__ __forceinline__ void step_terms(const Slot &s, const ActLds &A, int sl, float (&acc)[2][M],
                                            uint32_t hs0, uint32_t hs1) {
     const int jl = threadIdx.x & 7;
-    // the activation record of position m + 1 is read while position m is
-    // computed, and the first one while the weights are decoded, so the LDS
-    // latency hides behind arithmetic
+    // up to M = 8 the activation record of position m + 1 is read while
+    // position m is computed, and the first one while the weights are
+    // decoded, so the LDS latency hides behind arithmetic (above that the
+    // second record's registers are not free)
+    constexpr bool kPipe = M <= 8;
     ARec cur;
     read_act(cur, A, 0, sl);
     WDec d0, d1;
@@ -751,13 +759,18 @@ __device__ __forceinline__ void step_terms(const Slot &s, const ActLds &A, int s
 #pragma unroll
     for (int m = 0; m < M; m++) {
         ARec nxt;
-        if (m + 1 < M) read_act(nxt, A, m + 1, sl);
-        // keep the reads above the arithmetic that does not need them
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kPipe) {
+            if (m + 1 < M) read_act(nxt, A, m + 1, sl);
+            // keep the reads above the arithmetic that does not need them
+            __builtin_amdgcn_sched_barrier(0);
+        } else if (m > 0) {
+            read_act(cur, A, m, sl);
+        }
         const AExt ae = act_ext(cur);
         acc[0][m] = block_term<QT>(d0, cur, ae, acc[0][m]);
         acc[1][m] = block_term<QT>(d1, cur, ae, acc[1][m]);
-        if (m + 1 < M) cur = nxt;
+        if constexpr (kPipe)
+            if (m + 1 < M) cur = nxt;
     }
 }
 
@@ -795,7 +808,7 @@ __device__ __forceinline__ void put_partials(float *wp, float (&acc)[2][M], int 
 #pragma unroll
         for (int m = 0; m < M; m++) {
             const float v = group8_sum(acc[p][m]);
-            if (jl == 0) wp[((wave * 2 + mm) * M + m) * 16 + grp * 2 + p] = v;
+            if (jl == 0) wp[((wave * NMat<M>::value + mm) * M + m) * 16 + grp * 2 + p] = v;
             acc[p][m] = 0.0f;
         }
 }
@@ -946,17 +959,14 @@ __device__ __forceinline__ void dma_copy(uint8_t *dst, const uint8_t *src, int n
     }
 }
 
-// Copies the input chunk of a phase (codes, scales, code sums and, if the
-// input is RMS-normalised, its partials) into LDS with load-to-LDS
-// transfers and waits for them to land.
+// Copies the input chunk of a phase (codes, scales and code sums of every
+// position and, where they fit the launch's LDS, the input's RMS partials)
+// into LDS with load-to-LDS transfers and waits for them to land.
 template <int M, class PD>
 __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *act, Shared<M> &sh,
                                       unsigned long long *tr) {
     const int lane = threadIdx.x & 63;
     const int K = P.K, nsub = K >> 5, cs = g.cs;
-    const float *parts = P.in_parts;
-    const int n_parts = P.n_parts;
-    float *pd = reinterpret_cast<float *>(act + M * cs * 44);
     // three fields, each M rows: codes (row stride K), scales (nsub floats),
     // code sums (K / 16 ints); the LDS rows are contiguous, field after field
 #pragma unroll 1
@@ -970,7 +980,8 @@ __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *ac
 #pragma unroll 1
         for (int m = 0; m < M; m++) dma_copy(dst + m * row, src + m * sstride, row);
     }
-    if (parts) dma_copy(reinterpret_cast<uint8_t *>(pd), reinterpret_cast<const uint8_t *>(parts), M * n_parts * 4);
+    if (P.in_parts && P.parts_lds)
+        dma_copy(act + M * cs * kActRec, reinterpret_cast<const uint8_t *>(P.in_parts), M * P.n_parts * 4);
     if (tr && lane == 0) tr[12] = now();
     // the transfers have written LDS once this wave's loads are complete
     __builtin_amdgcn_s_waitcnt(0);
@@ -980,23 +991,36 @@ __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *ac
 // The RMS factors of the staged input (only the control wave reads them, in
 // the unit's finish, so they are formed after the compute waves are let go):
 // lane l adds partials l, l + 64, ... in order, then wave_sum (a fixed order
-// that depends only on the number of partials).
+// that depends only on the number of partials).  The partials come from LDS
+// where they were staged, else from global memory, a position's loads all
+// issued before the first add.
 template <int M, class PD>
 __device__ __forceinline__ void stage_rscale(const PD &P, const UnitPos &g, const uint8_t *act, Shared<M> &sh) {
     const int lane = threadIdx.x & 63;
     const int K = P.K, n_parts = P.n_parts;
-    const float *pd = reinterpret_cast<const float *>(act + M * g.cs * 44);
-    const bool parts = P.in_parts != nullptr;
+    if (!P.in_parts) {
+        if (lane < M) sh.rscale[lane] = 1.0f;
+        return;
+    }
+    const float *lp = reinterpret_cast<const float *>(act + M * g.cs * kActRec);
 #pragma unroll 1
     for (int m = 0; m < M; m++) {
-        float r = 1.0f;
-        if (parts) {
-            float t = 0.0f;
-            for (int i = lane; i < n_parts; i += 64) t += pd[m * n_parts + i];
-            const float tot = wave_sum(t);
-            r = 1.0f / sqrtf(tot / static_cast<float>(K) + P.eps);
+        float t = 0.0f;
+        if (P.parts_lds) {
+            for (int i = lane; i < n_parts; i += 64) t += lp[m * n_parts + i];
+        } else {
+            const float *gp = P.in_parts + m * n_parts;
+            float v[kPartsPerLane];
+#pragma unroll
+            for (int k = 0; k < kPartsPerLane; k++) {
+                const int i = lane + 64 * k;
+                v[k] = i < n_parts ? gld(gp + i) : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kPartsPerLane; k++) t += v[k];
         }
-        if (lane == 0) sh.rscale[m] = r;
+        const float tot = wave_sum(t);
+        if (lane == 0) sh.rscale[m] = 1.0f / sqrtf(tot / static_cast<float>(K) + P.eps);
     }
 }
 
@@ -1139,12 +1163,13 @@ __device__ __forceinline__ void finish_issue(const PD &P, uint32_t u, const floa
 #pragma unroll
     for (int k = 0; k < (M + 1) / 2; k++) {
         const int m = min(h + 2 * k, M - 1);
-        float a = wp[((hr * 2 + 0) * M + m) * 16 + rr];
-        float c = wp[((hr * 2 + 1) * M + m) * 16 + rr];
+        constexpr int NM = NMat<M>::value;
+        float a = wp[((hr * NM + 0) * M + m) * 16 + rr];
+        float c = wp[((hr * NM + NM - 1) * M + m) * 16 + rr];
 #pragma unroll
         for (int q = 1; q < kStepParts; q++) {
-            a += wp[(((hr + 2 * q) * 2 + 0) * M + m) * 16 + rr];
-            c += wp[(((hr + 2 * q) * 2 + 1) * M + m) * 16 + rr];
+            a += wp[(((hr + 2 * q) * NM + 0) * M + m) * 16 + rr];
+            c += wp[(((hr + 2 * q) * NM + NM - 1) * M + m) * 16 + rr];
         }
         v0.v[k] = a;
         v1.v[k] = c;

@@ -76,6 +76,7 @@ struct PhaseDesc {
     const int32_t *as16;
     const float *in_parts;
     int32_t n_parts;
+    int32_t parts_lds;        // 1: the partials are staged into LDS after the chunk
     float eps;
     float *y[3];
     int32_t ep_mode, ep_src;
