@@ -9,6 +9,7 @@ import pytest
 
 import synth
 import gguf_encode as ge
+import interval
 
 pytestmark = pytest.mark.gpu
 
@@ -196,25 +197,6 @@ def test_shared_input_three_matrices(gu, orc):
 
 
 # ------------------------------------------------------------------ a4 epilogue
-def _check_requant(orc, v64, gamma, q_gpu, d_gpu, s16_gpu, ss_gpu):
-    """Codes of Q8A32(v * gamma) may differ from the oracle's only where
-    the fp32 value sits within rounding of a half-way point."""
-    v32 = v64.astype(np.float32)
-    q, d, s16, _ = orc.quantize_act(v32, gamma)
-    assert np.allclose(d_gpu, d, rtol=4e-5, atol=0)
-    diff = q_gpu.astype(np.int32) - q.astype(np.int32)
-    assert np.abs(diff).max(initial=0) <= 1
-    frac = np.count_nonzero(diff) / diff.size
-    assert frac < 2e-3, frac
-    if np.count_nonzero(diff):
-        vg = (v32 * gamma).astype(np.float64)
-        pos = vg / np.repeat(d.astype(np.float64), 32, axis=1)
-        near = np.abs(np.abs(pos - np.trunc(pos)) - 0.5)
-        assert np.all(near[diff != 0] < 1e-3)
-    ref_ss = (v64 ** 2).reshape(v64.shape[0], -1, 32).sum(2)
-    assert np.allclose(ss_gpu, ref_ss, rtol=1e-4)
-
-
 @pytest.mark.parametrize("qt", [12, 14])
 def test_epilogue_quant_and_rms_fold(gu, orc, qt):
     import speculative_decoding_verification_amd as sv
@@ -237,13 +219,18 @@ def test_epilogue_quant_and_rms_fold(gu, orc, qt):
     y64, T = orc.matvec(qt, raw, K, q, d, scale=r)
     yg = gu.host(y).astype(np.float64)
     assert np.all(np.abs(yg - y64) <= TOL * T)
-    _check_requant(orc, y64, gamma, gu.host(out.q), gu.host(out.d), gu.host(out.s16), gu.host(out.sumsq))
+    interval.check_requant(y64, TOL * T, gamma, gu.host(out.q), gu.host(out.d), gu.host(out.s16),
+                           gu.host(out.sumsq))
 
 
-def test_epilogue_pair(gu, orc):
+@pytest.mark.parametrize("N,K,M", [(512, 2560, 5), (512, 2560, 9), (9728, 2560, 16), (2048, 6144, 9)])
+def test_epilogue_pair(gu, orc, N, K, M):
+    """Gate/up pair with the product's requantisation: fused units up to
+    M = 8, two matrices joined through the K-split partials above (M = 9,
+    16), a balanced decomposition at 9728 rows, two K chunks at K = 6144."""
     import speculative_decoding_verification_amd as sv
     import torch
-    qt, N, K, M = 12, 512, 2560, 5
+    qt = 12
     rg = synth.gguf_weights(qt, N, K, 61, "g")
     ru = synth.gguf_weights(qt, N, K, 61, "u")
     Wg, bg = gu.upload_weight(qt, rg, K)
@@ -261,10 +248,19 @@ def test_epilogue_pair(gu, orc):
     u64, Tu = orc.matvec(qt, ru, K, q, d)
     hg, hu = gu.host(yg), gu.host(yu)
     assert np.all(np.abs(hg - g64) <= TOL * Tg) and np.all(np.abs(hu - u64) <= TOL * Tu)
-    prod = (hg * hu).astype(np.float64)   # the product the pair epilogue quantises, fp32
-    ref = g64 * u64
-    assert np.all(np.abs(prod - ref) <= 3 * TOL * (Tg * np.abs(u64) + Tu * np.abs(g64)) + 1e-30)
-    _check_requant(orc, ref, gamma, gu.host(out.q), gu.host(out.d), gu.host(out.s16), gu.host(out.sumsq))
+    # the product the epilogue quantises is fp32(g) * fp32(u) of the outputs
+    interval.check_requant(g64 * u64, interval.pair_bound(g64, Tg, u64, Tu, TOL), gamma, gu.host(out.q),
+                           gu.host(out.d), gu.host(out.s16), gu.host(out.sumsq))
+    # each row of an M-row call equals the same row alone
+    if M > 1:
+        b1 = gu.quantize(x[M - 1:M])
+        out1 = gu.ActBuf(1, N)
+        y1 = [gu.empty((1, N), torch.float32) for _ in range(2)]
+        ep1 = sv.epilogue(sv.SV_EP_PAIR, out1.q, out1.d, out1.s16, out1.sumsq, gamma=gu.dev(gamma))
+        sv.verify_matvec([Wg, Wu], b1.act(), y1, ep1)
+        assert np.array_equal(gu.host(y1[0]).view(np.uint32), hg[M - 1:].view(np.uint32))
+        assert np.array_equal(gu.host(out1.q), gu.host(out.q)[M - 1:])
+        assert np.array_equal(gu.host(out1.d).view(np.uint32), gu.host(out.d)[M - 1:].view(np.uint32))
 
 
 # ------------------------------------------------------------------ a6 / a9 head
