@@ -395,3 +395,146 @@ def test_accept_rejection(gu, orc, V, T, mode, seed):
         else:
             uncertified += 1
     assert uncertified <= 1
+
+
+def _softmax64(z):
+    e = np.exp(z.astype(np.float64) - z.astype(np.float64).max())
+    return e / e.sum()
+
+
+def _rejection_both(gu, orc, z, drafts, u, q, T=1.0):
+    """GPU and oracle acceptance on the same inputs; returns (gpu, oracle,
+    oracle margins).  For the general drafter at K = 0 the GPU gets a
+    one-row q it never reads (a null q selects the certain drafter)."""
+    import speculative_decoding_verification_amd as sv
+    import torch
+    K, V = len(drafts), z.shape[1]
+    ws = gu.empty((sv.accept_workspace_bytes(V, K),), torch.uint8)
+    out = gu.zeros((K + 2,), torch.int32)
+    dd = np.asarray(drafts, np.int32)
+    qg = None if q is None else gu.dev(q if K else np.zeros((1, V), np.float32))
+    sv.accept_rejection(gu.dev(z), gu.dev(dd) if K else None, gu.dev(u), out, ws, temperature=T, q=qg)
+    want, mg = orc.accept_rejection(z, dd, u, T, q=None if q is None else np.asarray(q, np.float32).reshape(K, V),
+                                    with_margin=True)
+    return gu.host(out), want, mg
+
+
+def test_accept_rejection_edges(gu, orc):
+    """Edge cases of the rejection rule (micrologics, "Mathematical Integrity:
+    Rejection Sampling for LLMs"), GPU against oracle bit for bit."""
+    rng = np.random.default_rng(17)
+    V = 97
+    # K = 0: one token from row 0; the certain drafter draws it with u[0][0],
+    # the general one as the bonus with u[0][1]
+    for t in range(40):
+        z = (rng.standard_normal((1, V)) * 2).astype(np.float32)
+        u = rng.random((1, 2))
+        for q in (None, np.zeros((0, V), np.float32)):
+            got, want, _ = _rejection_both(gu, orc, z, [], u, q)
+            assert np.array_equal(got, want) and got[0] == 0
+    # q = p (p exactly representable): every draft is kept
+    z = np.tile(np.log(np.array([1, 1, 2, 4], np.float64)).astype(np.float32), (5, 1))
+    p = _softmax64(z[0]).astype(np.float32)
+    for t in range(100):
+        drafts = rng.integers(0, 4, 4)
+        got, want, _ = _rejection_both(gu, orc, z, drafts, rng.random((5, 2)), np.tile(p, (4, 1)))
+        assert np.array_equal(got, want) and got[0] == 4
+    # disjoint supports: p on 0..3, q on 4..7: the first draft is rejected
+    # and the token comes from the residual, which is p
+    z = np.full((3, 8), -3e38, np.float32)
+    z[:, :4] = 0.0
+    q = np.zeros((2, 8), np.float32)
+    q[:, 4:] = 0.25
+    for t in range(100):
+        got, want, _ = _rejection_both(gu, orc, z, rng.integers(4, 8, 2), rng.random((3, 2)), q)
+        assert np.array_equal(got, want) and got[0] == 0 and got[1] < 4
+    # R = 0: q = 2p leaves no residual mass; a rejection (u0 q(x) >= p(x),
+    # i.e. u0 >= 1/2) then draws from p itself with u[i][1]
+    rejected = 0
+    for t in range(200):
+        z = (rng.standard_normal((3, 50)) * 1.5).astype(np.float32)
+        q = np.stack([(2 * _softmax64(z[i])).astype(np.float32) for i in range(2)])
+        drafts = rng.integers(0, 50, 2)
+        u = rng.random((3, 2))
+        u[:, 0] = np.where(np.abs(u[:, 0] - 0.5) < 1e-6, 0.25, u[:, 0])
+        got, want, mg = _rejection_both(gu, orc, z, drafts, u, q)
+        assert np.all(mg[:want[0] + 1] > 1e-9)
+        assert np.array_equal(got, want)
+        rejected += int(want[0] < 2)
+    assert rejected > 50
+
+
+def test_restricted_drafter_head_vs_oracle(gu, orc):
+    """Q8_0 drafter head over 32768 seeded distinct tokens plus 256 appended
+    tokens outside that set, in arbitrary order (OpenJet, "Cheap drafting,
+    careful state management": a fixed bundle of frequent tokens with the
+    sequence's own tokens added as they appear), read from a 151936-token
+    Q8_0 head through row_ids.  Logits against the oracle's row_ids path
+    within 1e-5 * T, bit-identical to the same rows of the full head, and
+    the argmax position checked by interval on every row."""
+    import speculative_decoding_verification_amd as sv
+    import torch
+    qt, V, K = 8, 151936, 5120
+    raw = synth.gguf_weights(qt, V, K, seed=91)
+    H, hb = gu.upload_weight(qt, raw, K)
+    bundle = synth.token_ids(32768, V, seed=92, distinct=True)
+    rest = np.setdiff1d(np.arange(V), bundle)
+    tail = synth.stream(93, "tail").permutation(rest)[:256]
+    ids = np.concatenate([bundle, tail]).astype(np.int32)
+    ids_d = gu.dev(ids)
+    for M in (5, 16):
+        x = synth.activations(M, K, seed=94)
+        b = gu.quantize(x)
+        part = gu.empty((M, ids.size), torch.float32)
+        am = gu.zeros((M,), torch.int64)
+        sv.head_logits(H, b.act(), part, am, row_ids=ids_d)
+        full = gu.empty((M, V), torch.float32)
+        sv.head_logits(H, b.act(), full, None)
+        pl, fl = gu.host(part), gu.host(full)
+        assert np.array_equal(pl.view(np.uint32), fl[:, ids].view(np.uint32))
+        q, d, _ = _oracle_act(orc, x)
+        y64, T = orc.matvec(qt, raw, K, q, d, row_ids=ids)
+        assert np.all(np.abs(pl - y64) <= TOL * T)
+        pos = np.array([sv.argmax_index(int(p)) for p in gu.host(am).view(np.uint64)])
+        assert np.array_equal(pos, pl.argmax(1))
+        assert interval.check_winner(pos, y64, TOL * T) == M
+
+
+def test_restricted_head_tie_rule(gu, orc):
+    """Equal logits resolve to the lowest position in the id list, not the
+    lowest token id: a bundle row beats an appended row it ties with, and of
+    two tied appended rows the earlier one wins although its token id is the
+    larger.  The tied rows are byte copies of one dominant row (scale 1, codes
+    127 times the sign of the input's codes)."""
+    import speculative_decoding_verification_amd as sv
+    import torch
+    qt, V, K = 8, 4096, 1024
+    x = synth.activations(1, K, seed=95)
+    xq = orc.quantize_act(x)[0][0]
+    nb = K // 32
+    dom = ge.encode_q8_0(np.full(nb, int(ge.half_bits(1.0)), np.uint16),
+                         (np.where(xq >= 0, 127, -127)).reshape(nb, 32))
+    bundle = synth.token_ids(3000, V, seed=96, distinct=True)
+    rest = np.setdiff1d(np.arange(V), bundle)
+    tail = synth.stream(97, "tail").permutation(rest)[:256]
+    ids = np.concatenate([bundle, tail]).astype(np.int32)
+    # tail positions a < b with ids[a] > ids[b]
+    a = next(i for i in range(3000, ids.size - 1) if ids[i] > ids[i + 1])
+    b = a + 1
+    cases = [((10, a), 10), ((a, b), a)]
+    b_act = gu.quantize(x)
+    for (p0, p1), want in cases:
+        raw = synth.gguf_weights(qt, V, K, seed=98)
+        raw[ids[p0]] = dom
+        raw[ids[p1]] = dom
+        H, hb = gu.upload_weight(qt, raw, K)
+        part = gu.empty((1, ids.size), torch.float32)
+        am = gu.zeros((1,), torch.int64)
+        sv.head_logits(H, b_act.act(), part, am, row_ids=gu.dev(ids))
+        pl = gu.host(part)[0]
+        assert pl[p0] == pl[p1] and pl[p0] == pl.max()
+        assert sv.argmax_index(int(gu.host(am).view(np.uint64)[0])) == want
+        # greedy acceptance maps the position to its token
+        out = gu.zeros((2,), torch.int32)
+        sv.accept_greedy(am, None, out, ids.size, row_ids=gu.dev(ids))
+        assert list(gu.host(out)) == [0, int(ids[want])]
