@@ -327,6 +327,24 @@ int sv_accept_rejection(const float *logits, int64_t V, const float *q, const in
                         int32_t K, const double *u, float temperature, void *workspace,
                         size_t ws_bytes, int32_t *out, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sv_accept_rejection with
+ * the same arguments minus the workspace, run on a static scratch array of
+ * sv_accept_noalloc_max_bytes() bytes (256 KiB) that each GPU the library
+ * runs on holds until the process ends.  The round must fit it:
+ * sv_accept_workspace_bytes(V, K) <= that size (V up to 860160 tokens at
+ * K = 15, more for smaller K), else SV_ERR_WORKSPACE before any runtime
+ * call.  It allocates nothing; the first call on a device looks up the
+ * scratch's address there.  Every call on one GPU shares its scratch, so
+ * calls that overlap on one GPU (on different streams, or from several
+ * threads without ordering) race and must not be made; the scratch keeps
+ * the last call's contents, and a round writes every entry it reads.
+ * Results equal sv_accept_rejection's bit for bit. */
+size_t sv_accept_noalloc_max_bytes(void);
+int sv_accept_rejection_noalloc(const float *logits, int64_t V, const float *q, const int32_t *drafts,
+                                int32_t K, const double *u, float temperature, int32_t *out,
+                                void *stream);
+
 /* ------------------------------------------------------------------ */
 /* Measurement aid (not a step of the pass).                           */
 /* ------------------------------------------------------------------ */

@@ -26,7 +26,7 @@ EXPORTS = [
     "sv_quantize_act_q8", "sv_matvec_workspace_bytes", "sv_verify_matvec", "sv_head_workspace_bytes",
     "sv_head_logits", "sv_argmax_index", "sv_pass_workspace_bytes", "sv_pass_create", "sv_pass_run",
     "sv_pass_status", "sv_pass_trace", "sv_pass_destroy", "sv_accept_greedy", "sv_accept_workspace_bytes",
-    "sv_accept_rejection", "sv_read_bandwidth",
+    "sv_accept_rejection", "sv_accept_noalloc_max_bytes", "sv_accept_rejection_noalloc", "sv_read_bandwidth",
 ]
 
 
@@ -102,9 +102,13 @@ def lib():
         L.sv_accept_workspace_bytes.restype = ctypes.c_size_t
         L.sv_accept_workspace_bytes.argtypes = [i64, i32]
         L.sv_accept_rejection.argtypes = [P, i64, P, P, i32, P, ctypes.c_float, P, ctypes.c_size_t, P, P]
+        L.sv_accept_noalloc_max_bytes.restype = ctypes.c_size_t
+        L.sv_accept_noalloc_max_bytes.argtypes = []
+        L.sv_accept_rejection_noalloc.argtypes = [P, i64, P, P, i32, P, ctypes.c_float, P, P]
         L.sv_read_bandwidth.argtypes = [P, ctypes.c_size_t, P, i32, P]
         for f in ("sv_repack_weights", "sv_unpack_weights", "sv_quantize_act_q8", "sv_verify_matvec",
-                  "sv_head_logits", "sv_accept_greedy", "sv_accept_rejection", "sv_pass_create",
+                  "sv_head_logits", "sv_accept_greedy", "sv_accept_rejection", "sv_accept_rejection_noalloc",
+                  "sv_pass_create",
                   "sv_pass_run", "sv_pass_status", "sv_read_bandwidth"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -307,6 +311,19 @@ def accept_rejection(logits, drafts, u, out, workspace, temperature=1.0, q=None,
     _check(lib().sv_accept_rejection(_ptr(logits), V, _ptr(q), _ptr(drafts), K, _ptr(u), float(temperature),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
                                      _stream(stream)))
+
+
+def accept_noalloc_max_bytes() -> int:
+    return int(lib().sv_accept_noalloc_max_bytes())
+
+
+def accept_rejection_noalloc(logits, drafts, u, out, temperature=1.0, q=None, stream=None):
+    """accept_rejection on the library's static scratch (no workspace, no
+    allocation); calls that overlap on one GPU must not be made."""
+    V = logits.shape[-1]
+    K = 0 if drafts is None else drafts.numel()
+    _check(lib().sv_accept_rejection_noalloc(_ptr(logits), V, _ptr(q), _ptr(drafts), K, _ptr(u),
+                                             float(temperature), _ptr(out), _stream(stream)))
 
 
 def read_bandwidth(src, sink, stream=None):

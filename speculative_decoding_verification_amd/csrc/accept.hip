@@ -21,6 +21,8 @@
 // differ from a strictly sequential fp64 sum only by rounding (~1e-11
 // relative for V ~ 1.5e5), i.e. only when a uniform falls that close to a
 // decision boundary.
+#include <mutex>
+
 #include "sv_internal.h"
 
 namespace sv {
@@ -321,33 +323,96 @@ extern "C" int sv_accept_greedy(const uint64_t *argmax, const int32_t *row_ids, 
     return sv::hip_check(hipGetLastError(), "accept_greedy launch");
 }
 
-extern "C" int sv_accept_rejection(const float *logits, int64_t V, const float *q, const int32_t *drafts, int32_t K,
-                                   const double *u, float temperature, void *workspace, size_t ws_bytes, int32_t *out,
-                                   void *stream) {
-    SV_REQUIRE(logits && u && out && workspace && (K == 0 || drafts), SV_ERR_ARG, "accept_rejection: NULL buffer");
-    SV_REQUIRE(K >= 0 && K < SV_MAX_M, SV_ERR_ARG, "accept_rejection: K must be in [0, 15]");
-    SV_REQUIRE(V >= 1 && V < (1ll << 31), SV_ERR_SHAPE, "accept_rejection: V out of range");
-    SV_REQUIRE(temperature > 0.0f, SV_ERR_ARG, "accept_rejection: temperature must be > 0");
+namespace sv {
+
+// The rejection round on a given scratch area (the caller's workspace, or
+// the static scratch of the allocation-free entry point).
+static int rejection_round(const char *name, const float *logits, int64_t V, const float *q, const int32_t *drafts,
+                           int32_t K, const double *u, float temperature, void *workspace, size_t ws_bytes,
+                           int32_t *out, void *stream) {
+    const std::string who(name);
+    SV_REQUIRE(logits && u && out && workspace && (K == 0 || drafts), SV_ERR_ARG, who + ": NULL buffer");
+    SV_REQUIRE(K >= 0 && K < SV_MAX_M, SV_ERR_ARG, who + ": K must be in [0, 15]");
+    SV_REQUIRE(V >= 1 && V < (1ll << 31), SV_ERR_SHAPE, who + ": V out of range");
+    SV_REQUIRE(temperature > 0.0f, SV_ERR_ARG, who + ": temperature must be > 0");
     size_t o_cmax, o_csum, o_rsum;
-    const size_t need = sv::ws_layout(V, K, &o_cmax, &o_csum, &o_rsum);
-    SV_REQUIRE(ws_bytes >= need, SV_ERR_WORKSPACE,
-               "accept_rejection: workspace needs " + std::to_string(need) + " bytes");
-    SV_REQUIRE(sv::aligned(workspace, 8) && sv::aligned(logits, 4) && sv::aligned(u, 8) && sv::aligned(out, 4) &&
-                   (!q || sv::aligned(q, 4)) && (!drafts || sv::aligned(drafts, 4)),
-               SV_ERR_ALIGN, "accept_rejection: alignment");
+    const size_t need = ws_layout(V, K, &o_cmax, &o_csum, &o_rsum);
+    SV_REQUIRE(ws_bytes >= need, SV_ERR_WORKSPACE, who + ": workspace needs " + std::to_string(need) + " bytes");
+    SV_REQUIRE(aligned(workspace, 8) && aligned(logits, 4) && aligned(u, 8) && aligned(out, 4) &&
+                   (!q || aligned(q, 4)) && (!drafts || aligned(drafts, 4)),
+               SV_ERR_ALIGN, who + ": alignment");
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     float *cmax = reinterpret_cast<float *>(ws + o_cmax);
     double *csum = reinterpret_cast<double *>(ws + o_csum);
     double *rsum = reinterpret_cast<double *>(ws + o_rsum);
-    const int C = static_cast<int>((V + sv::kCh - 1) / sv::kCh);
+    const int C = static_cast<int>((V + kCh - 1) / kCh);
     const double T = static_cast<double>(temperature);
-    hipStream_t st = sv::as_stream(stream);
-    hipLaunchKernelGGL(sv::acc_chunk_max, dim3(C, K + 1), dim3(sv::kCh), 0, st, logits, V, C, cmax);
-    hipLaunchKernelGGL(sv::acc_chunk_sum, dim3(C, K + 1), dim3(sv::kCh), 0, st, logits, V, C, cmax, T, csum);
+    hipStream_t st = as_stream(stream);
+    hipLaunchKernelGGL(acc_chunk_max, dim3(C, K + 1), dim3(kCh), 0, st, logits, V, C, cmax);
+    hipLaunchKernelGGL(acc_chunk_sum, dim3(C, K + 1), dim3(kCh), 0, st, logits, V, C, cmax, T, csum);
     if (q && K > 0)
-        hipLaunchKernelGGL(sv::acc_chunk_resid, dim3(C, K), dim3(sv::kCh), 0, st, logits, q, V, C, cmax, csum, T,
-                           rsum);
-    hipLaunchKernelGGL(sv::acc_decide, dim3(1), dim3(sv::kCh), 0, st, logits, q, V, C, drafts, K, u, T, cmax, csum,
-                       rsum, out);
-    return sv::hip_check(hipGetLastError(), "accept_rejection launch");
+        hipLaunchKernelGGL(acc_chunk_resid, dim3(C, K), dim3(kCh), 0, st, logits, q, V, C, cmax, csum, T, rsum);
+    hipLaunchKernelGGL(acc_decide, dim3(1), dim3(kCh), 0, st, logits, q, V, C, drafts, K, u, T, cmax, csum, rsum,
+                       out);
+    return hip_check(hipGetLastError(), (who + " launch").c_str());
+}
+
+// Scratch of the allocation-free entry point: chunk maxima and chunk sums of
+// one round, every entry written before it is read within the round, so no
+// clearing is needed.  Each GPU holds its own copy until the process ends;
+// in host code the array's name only stands in for it, and its device
+// address comes from hipGetSymbolAddress with that device current.
+constexpr size_t kScratchBytes = 256 * 1024;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch[kMaxDevices];
+
+static int device_scratch(void **out) {
+    int dev = 0;
+    int rc = hip_check(hipGetDevice(&dev), "accept_rejection_noalloc: device query");
+    if (rc) return rc;
+    SV_REQUIRE(dev >= 0 && dev < kMaxDevices, SV_ERR_ARG, "accept_rejection_noalloc: device index above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        rc = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "accept_rejection_noalloc: scratch address");
+        if (rc) return rc;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return SV_OK;
+}
+
+}  // namespace sv
+
+extern "C" int sv_accept_rejection(const float *logits, int64_t V, const float *q, const int32_t *drafts, int32_t K,
+                                   const double *u, float temperature, void *workspace, size_t ws_bytes, int32_t *out,
+                                   void *stream) {
+    return sv::rejection_round("accept_rejection", logits, V, q, drafts, K, u, temperature, workspace, ws_bytes, out,
+                               stream);
+}
+
+extern "C" size_t sv_accept_noalloc_max_bytes(void) { return sv::kScratchBytes; }
+
+extern "C" int sv_accept_rejection_noalloc(const float *logits, int64_t V, const float *q, const int32_t *drafts,
+                                           int32_t K, const double *u, float temperature, int32_t *out,
+                                           void *stream) {
+    using namespace sv;
+    // sizes first, on the host alone: a round too large for the scratch is
+    // refused before any runtime call
+    SV_REQUIRE(K >= 0 && K < SV_MAX_M, SV_ERR_ARG, "accept_rejection_noalloc: K must be in [0, 15]");
+    SV_REQUIRE(V >= 1 && V < (1ll << 31), SV_ERR_SHAPE, "accept_rejection_noalloc: V out of range");
+    size_t a, b, c;
+    const size_t need = ws_layout(V, K, &a, &b, &c);
+    SV_REQUIRE(need <= kScratchBytes, SV_ERR_WORKSPACE,
+               "accept_rejection_noalloc: V = " + std::to_string(V) + ", K = " + std::to_string(K) + " needs " +
+                   std::to_string(need) + " bytes of scratch; the static scratch holds " +
+                   std::to_string(kScratchBytes) + " (use sv_accept_rejection with a workspace)");
+    void *ws = nullptr;
+    const int rc = device_scratch(&ws);
+    if (rc) return rc;
+    return rejection_round("accept_rejection_noalloc", logits, V, q, drafts, K, u, temperature, ws, kScratchBytes,
+                           out, stream);
 }

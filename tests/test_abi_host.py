@@ -160,6 +160,17 @@ def test_head_and_accept_rejects():
          sv.SV_ERR_WORKSPACE)
     _err(L.sv_accept_rejection(FAKE, 0, None, FAKE, 4, FAKE, ctypes.c_float(1.0), FAKE, ws, FAKE, None),
          sv.SV_ERR_SHAPE)
+    # the allocation-free variant refuses a round larger than its static
+    # scratch before any runtime call
+    cap = sv.accept_noalloc_max_bytes()
+    assert cap == 256 * 1024 and sv.accept_workspace_bytes(860160, 15) <= cap
+    assert sv.accept_workspace_bytes(860161, 15) > cap
+    _err(L.sv_accept_rejection_noalloc(FAKE, 860161, None, FAKE, 15, FAKE, ctypes.c_float(1.0), FAKE, None),
+         sv.SV_ERR_WORKSPACE)
+    _err(L.sv_accept_rejection_noalloc(FAKE, 151936, None, FAKE, 16, FAKE, ctypes.c_float(1.0), FAKE, None),
+         sv.SV_ERR_ARG)
+    _err(L.sv_accept_rejection_noalloc(FAKE, 0, None, FAKE, 4, FAKE, ctypes.c_float(1.0), FAKE, None),
+         sv.SV_ERR_SHAPE)
 
 
 def _chunking(rows, cols, balance=True, grid=256, max_s=8):
