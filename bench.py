@@ -258,7 +258,16 @@ def recorded_traffic(config, M):
         return None
 
 
+def _under_profiler():
+    return any(k.startswith(("ROCPROF", "ROCPROFILER")) for k in os.environ)
+
+
 def _smi():
+    # rocm-smi is a launcher that replaces itself with python; under
+    # rocprofv3 every child process has the GPU initialised by the
+    # profiler's library first, so no smi reading is taken there
+    if _under_profiler():
+        return {"skipped": "under rocprofv3"}
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showtemp", "--json"],
                            capture_output=True, text=True, timeout=30)
