@@ -935,27 +935,43 @@ __device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target,
 // (or 4 l), so the LDS destination of each instruction is uniform.  The
 // loops stay rolled: this code runs once per staged chunk, after a wait, so
 // its length (instruction-cache misses), not its loop overhead, is what
-// costs.
+// costs.  Whole-wave transfers run in a loop with a uniform trip count (no
+// per-lane masking inside it), then one partial transfer takes the rest.
 __device__ __forceinline__ void dma_copy(uint8_t *dst, const uint8_t *src, int n) {
-    const int lane = threadIdx.x & 63;
-    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | static_cast<uintptr_t>(n)) & 15) == 0) {
-        const int n16 = n >> 4;
+    const uint32_t lane = threadIdx.x & 63;
+    // size and both bases are wave-uniform: scalar loop control, and the
+    // LDS address goes to M0 without a lane read each time
+    const int nu = __builtin_amdgcn_readfirstlane(n);
+    const uint32_t d0 = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>((uint32_t)(uintptr_t)(SV_AS3 uint8_t *)dst)));
+    // readfirstlane returns a signed int: each half goes through uint32_t
+    // before it is widened, so the low half is not sign-extended
+    const uint64_t sa = reinterpret_cast<uint64_t>(src);
+    const uint32_t slo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sa & 0xFFFFFFFFu)));
+    const uint32_t shi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sa >> 32)));
+    const uint64_t s0 = static_cast<uint64_t>(slo) | (static_cast<uint64_t>(shi) << 32);
+    if (((s0 | d0 | static_cast<uint64_t>(nu)) & 15) == 0) {
+        const int full = nu >> 10;                 // 1 KiB per whole-wave 16-byte transfer
+        const int rest = (nu >> 4) - (full << 6);  // 16-byte pieces after them
+        const uint64_t sl = s0 + lane * 16u;
 #pragma unroll 1
-        for (int k = 0; 64 * k < n16; k++) {
-            const int i = 64 * k + lane;
-            if (i < n16)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + i * 16),
-                                                 (SV_AS3 void *)(dst + 64 * k * 16), 16, 0, 0);
-        }
+        for (int k = 0; k < full; k++)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(sl + (static_cast<uint64_t>(k) << 10)),
+                                             (SV_AS3 void *)static_cast<uintptr_t>(d0 + (k << 10)), 16, 0, 0);
+        if (rest > 0 && static_cast<int>(lane) < rest)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(sl + (static_cast<uint64_t>(full) << 10)),
+                                             (SV_AS3 void *)static_cast<uintptr_t>(d0 + (full << 10)), 16, 0, 0);
     } else {
-        const int n4 = n >> 2;
+        const int full = nu >> 8;                  // 256 bytes per whole-wave 4-byte transfer
+        const int rest = (nu >> 2) - (full << 6);
+        const uint64_t sl = s0 + lane * 4u;
 #pragma unroll 1
-        for (int k = 0; 64 * k < n4; k++) {
-            const int i = 64 * k + lane;
-            if (i < n4)
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + i * 4),
-                                                 (SV_AS3 void *)(dst + 64 * k * 4), 4, 0, 0);
-        }
+        for (int k = 0; k < full; k++)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(sl + (static_cast<uint64_t>(k) << 8)),
+                                             (SV_AS3 void *)static_cast<uintptr_t>(d0 + (k << 8)), 4, 0, 0);
+        if (rest > 0 && static_cast<int>(lane) < rest)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(sl + (static_cast<uint64_t>(full) << 8)),
+                                             (SV_AS3 void *)static_cast<uintptr_t>(d0 + (full << 8)), 4, 0, 0);
     }
 }
 
