@@ -993,8 +993,13 @@ __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *ac
         const int64_t sstride = f == 0 ? K : (f == 1 ? nsub * 4 : (K >> 4) * 4);
         const int row = f == 0 ? cs * 32 : (f == 1 ? cs * 4 : cs * 8);
         uint8_t *dst = act + (f == 0 ? 0 : (f == 1 ? M * cs * 32 : M * cs * 36));
+        if (sstride == row) {
+            // the chunk is the whole row: the M rows are contiguous in memory
+            dma_copy(dst, src, M * row);
+        } else {
 #pragma unroll 1
-        for (int m = 0; m < M; m++) dma_copy(dst + m * row, src + m * sstride, row);
+            for (int m = 0; m < M; m++) dma_copy(dst + m * row, src + m * sstride, row);
+        }
     }
     if (P.in_parts && P.parts_lds)
         dma_copy(act + M * cs * kActRec, reinterpret_cast<const uint8_t *>(P.in_parts), M * P.n_parts * 4);
