@@ -440,22 +440,28 @@ static int plan_pass(const sv_phase *phases, int32_t n_phases, std::vector<Phase
 }
 
 // The unit geometry of the device's unit_pos, for the host's schedule.
-static void host_unit_range(const PhaseDesc &P, uint32_t u, int &c0, int &c1, int &s_begin, int &cs) {
+static void host_unit_range(const PhaseDesc &P, uint32_t u, int &c0, int &c1, int &s_begin, int &cs, int &pb,
+                            int &pcs) {
     const int per_tile = P.per_tile, S = P.S, head = P.T1 * per_tile;
-    int chunk, nch;
+    int chunk, nch, parent;
     if (static_cast<int>(u) < head) {
         chunk = (static_cast<int>(u) % per_tile) % S;
         nch = S;
+        parent = chunk;
     } else {
         const int v = static_cast<int>(u) - head, f = P.S1 / S;
         const int rem = v % per_tile, q = v / per_tile;
-        chunk = f * (rem % S) + q % f;
+        parent = rem % S;
+        chunk = f * parent + q % f;
         nch = P.S1;
     }
     c0 = chunk * P.steps / nch;
     c1 = (chunk + 1) * P.steps / nch;
     s_begin = c0 * 8;
     cs = std::min((c1 - c0) * 8, P.K / 32 - s_begin);
+    const int p0 = parent * P.steps / S, p1 = (parent + 1) * P.steps / S;
+    pb = p0 * 8;
+    pcs = std::min((p1 - p0) * 8, P.K / 32 - pb);
 }
 
 // The order in which each workgroup of a pass runs units: the host
@@ -463,8 +469,10 @@ static void host_unit_range(const PhaseDesc &P, uint32_t u, int &c0, int &c1, in
 // bytes at one workgroup's streaming rate; a phase whose input another
 // phase writes starts a hand-off after that phase's last unit; staging an
 // input chunk costs a fixed time that grows with M) and gives every unit,
-// phase by phase in unit order, to the workgroup that can start it first,
-// preferring one that has its input chunk staged already.  So a phase that
+// phase by phase, to the workgroup that can start it first, preferring one
+// that has its input chunk staged already.  Within a phase the units go out
+// last to first, so the finely cut units of a balanced phase run first and
+// each workgroup ends the phase on a unit whose tile needs no combine.  So a phase that
 // no later phase waits for fills the workgroups a narrower phase leaves
 // idle, instead of delaying the phase after it.  Each workgroup's list is
 // in phase order and every wait is for an earlier phase, so the launch
@@ -483,9 +491,13 @@ static void schedule(const std::vector<PhaseDesc> &host, const std::vector<int> 
         const PhaseDesc &P = host[p];
         const double ready = producer[p] >= 0 ? phase_end[producer[p]] + hand : 0.0;
         const double row_bytes = static_cast<double>(P.bbytes) / 16.0 * (P.fused ? 2.0 : 1.0);
-        for (uint32_t u = 0; u < static_cast<uint32_t>(P.n_units); u++) {
-            int c0, c1, sb, cs;
-            host_unit_range(P, u, c0, c1, sb, cs);
+        // the units of tiles cut finer than S chunks (the last ones) are
+        // given out first: their partial sums are combined while the whole
+        // units run, so a phase ends on units that need no combine
+        for (int ui = P.n_units - 1; ui >= 0; ui--) {
+            const uint32_t u = static_cast<uint32_t>(ui);
+            int c0, c1, sb, cs, pb, pcs;
+            host_unit_range(P, u, c0, c1, sb, cs, pb, pcs);
             const double cost = kRows * (c1 - c0) * row_bytes / rate + unit_ovh;
             int best = 0;
             double best_t = 1e300;
@@ -501,8 +513,8 @@ static void schedule(const std::vector<PhaseDesc> &host, const std::vector<int> 
             }
             if (!best_staged) {
                 st_in[best] = P.aq;
-                st_b[best] = sb;
-                st_c[best] = cs;
+                st_b[best] = pb;
+                st_c[best] = pcs;
             }
             free_at[best] = best_t + cost;
             phase_end[p] = std::max(phase_end[p], free_at[best]);

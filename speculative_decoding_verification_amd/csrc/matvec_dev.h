@@ -136,6 +136,7 @@ __device__ __forceinline__ void unit_next(const Tab &tab, int, uint32_t, uint32_
 // one of the f finer chunks inside chunk c.
 struct UnitPos {
     int tile, chunk, nch, mat, c0, c1, s_begin, cs;
+    int pb, pcs;   // sub-blocks of the unit's K chunk at S chunks per tile (what is staged)
 };
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, uint32_t m, uint32_t sh) {
     return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> sh);
@@ -150,6 +151,15 @@ __device__ __forceinline__ UnitPos unit_pos(const PD &P, uint32_t u) {
     const uint32_t q = fdiv(v, P.div_pt.m, P.div_pt.sh), rem = v - q * per_tile;
     const uint32_t mat = fdiv(rem, P.div_S.m, P.div_S.sh), c = rem - mat * S;
     g.mat = static_cast<int>(mat);
+    const int nsub = P.K >> 5;
+    {
+        // the chunk of S the unit lies in (its own chunk unless the tile is
+        // cut finer): staging it serves every unit of that chunk
+        const int p0 = static_cast<int>(fdiv(c * steps, P.div_S.m, P.div_S.sh));
+        const int p1 = static_cast<int>(fdiv((c + 1) * steps, P.div_S.m, P.div_S.sh));
+        g.pb = p0 * 8;
+        g.pcs = min((p1 - p0) * 8, nsub - g.pb);
+    }
     uint32_t nch = S, chunk = c, tile = q;
     if (tail) {
         const uint32_t f = fdiv(static_cast<uint32_t>(P.S1), P.div_S.m, P.div_S.sh);
@@ -164,7 +174,6 @@ __device__ __forceinline__ UnitPos unit_pos(const PD &P, uint32_t u) {
     const uint32_t dm = tail ? P.div_S1.m : P.div_S.m, ds = tail ? P.div_S1.sh : P.div_S.sh;
     g.c0 = static_cast<int>(fdiv(chunk * steps, dm, ds));
     g.c1 = static_cast<int>(fdiv((chunk + 1) * steps, dm, ds));
-    const int nsub = P.K >> 5;
     g.s_begin = g.c0 * 8;
     g.cs = min((g.c1 - g.c0) * 8, nsub - g.s_begin);
     return g;
@@ -982,14 +991,15 @@ template <int M, class PD>
 __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *act, Shared<M> &sh,
                                       unsigned long long *tr) {
     const int lane = threadIdx.x & 63;
-    const int K = P.K, nsub = K >> 5, cs = g.cs;
-    // three fields, each M rows: codes (row stride K), scales (nsub floats),
+    const int K = P.K, nsub = K >> 5, cs = g.pcs, sb = g.pb;
+    // the unit's chunk of S (which holds the unit's own range); three
+    // fields, each M rows: codes (row stride K), scales (nsub floats),
     // code sums (K / 16 ints); the LDS rows are contiguous, field after field
 #pragma unroll 1
     for (int f = 0; f < 3; f++) {
-        const uint8_t *src = f == 0 ? reinterpret_cast<const uint8_t *>(P.aq) + static_cast<int64_t>(g.s_begin) * 32
-                             : f == 1 ? reinterpret_cast<const uint8_t *>(P.ad + g.s_begin)
-                                      : reinterpret_cast<const uint8_t *>(P.as16 + 2 * g.s_begin);
+        const uint8_t *src = f == 0 ? reinterpret_cast<const uint8_t *>(P.aq) + static_cast<int64_t>(sb) * 32
+                             : f == 1 ? reinterpret_cast<const uint8_t *>(P.ad + sb)
+                                      : reinterpret_cast<const uint8_t *>(P.as16 + 2 * sb);
         const int64_t sstride = f == 0 ? K : (f == 1 ? nsub * 4 : (K >> 4) * 4);
         const int row = f == 0 ? cs * 32 : (f == 1 ? cs * 4 : cs * 8);
         uint8_t *dst = act + (f == 0 ? 0 : (f == 1 ? M * cs * 32 : M * cs * 36));
@@ -1023,7 +1033,7 @@ __device__ __forceinline__ void stage_rscale(const PD &P, const UnitPos &g, cons
         if (lane < M) sh.rscale[lane] = 1.0f;
         return;
     }
-    const float *lp = reinterpret_cast<const float *>(act + M * g.cs * kActRec);
+    const float *lp = reinterpret_cast<const float *>(act + M * g.pcs * kActRec);
 #pragma unroll 1
     for (int m = 0; m < M; m++) {
         float t = 0.0f;
@@ -1351,8 +1361,8 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
                     if (tr && lane == 0) tr[2] = now();
                     st_q = aq;
                     st_parts = parts;
-                    st_begin = g.s_begin;
-                    st_cs = g.cs;
+                    st_begin = g.pb;
+                    st_cs = g.pcs;
                     fresh = true;
                 }
             }
