@@ -163,10 +163,11 @@ typedef struct {
  * the input A (q, k, v, or gate, up).  All W[j] have the same qtype and rows,
  * and cols = A->K (matrices of different formats on one input are separate
  * calls, or separate phases of a pass).  y[j] is [M][rows] fp32 or NULL.  ep may be NULL.
- * The K axis is cut into chunks whose number depends only on K; the fp32
- * combine order (sequential per lane, a fixed tree over a lane group, the
- * step halves and then the chunks added in order) depends only on K, never
- * on M, which makes every row
+ * The K axis is cut into chunks whose number depends only on K and the row
+ * count (the tiles of a last partial round of 256 tile-chunks are cut
+ * finer); the fp32 combine order (sequential per lane, a fixed tree over a
+ * lane group, the step quarters and then the chunks added in order) depends
+ * only on K and the row count, never on M, which makes every row
  * batch-invariant and every run deterministic.
  * workspace: sv_matvec_workspace_bytes(W, n_w, A) bytes, 256-byte aligned.
  * Its first 256 KiB hold tile counters that must be zero before the first
@@ -252,8 +253,10 @@ int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *workspace, si
                    sv_pass **out);
 
 /* Enqueues one pass on `stream`: a single persistent launch of as many
- * workgroups as the GPU holds at once (at most two per compute unit) that
- * works through the phases in order and leaves its counters reset for the
+ * workgroups as the GPU holds at once (one or two per compute unit, as the
+ * launch's registers and LDS allow; one at every M today), each working
+ * through its host-built list of units in phase order, that leaves its
+ * counters reset for the
  * next run.  Allocates nothing and records no memset, so it can be captured
  * in a graph.  Runs of one pass must not overlap, and the pass expects the
  * GPU to itself while it runs (its workgroups wait on each other; if
