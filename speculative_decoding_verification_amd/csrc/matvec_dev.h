@@ -984,11 +984,37 @@ __device__ __forceinline__ void dma_copy(uint8_t *dst, const uint8_t *src, int n
     }
 }
 
+// The phase fields that staging and the RMS factors read, taken from the
+// phase table before the wait for the input: the table is read through
+// vector loads, and one issued after the wait would put a memory round trip
+// in front of the staging transfers.
+struct StageIn {
+    const int8_t *aq;
+    const float *ad;
+    const int32_t *as16;
+    const float *parts;
+    int K, n_parts, parts_lds;
+    float eps;
+};
+template <class PD>
+__device__ __forceinline__ StageIn stage_in(const PD &P) {
+    StageIn s;
+    s.aq = P.aq;
+    s.ad = P.ad;
+    s.as16 = P.as16;
+    s.parts = P.in_parts;
+    s.K = P.K;
+    s.n_parts = P.n_parts;
+    s.parts_lds = P.parts_lds;
+    s.eps = P.eps;
+    return s;
+}
+
 // Copies the input chunk of a phase (codes, scales and code sums of every
 // position and, where they fit the launch's LDS, the input's RMS partials)
 // into LDS with load-to-LDS transfers and waits for them to land.
-template <int M, class PD>
-__device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *act, Shared<M> &sh,
+template <int M>
+__device__ __forceinline__ void stage(const StageIn &P, const UnitPos &g, uint8_t *act, Shared<M> &sh,
                                       unsigned long long *tr) {
     const int lane = threadIdx.x & 63;
     const int K = P.K, nsub = K >> 5, cs = g.pcs, sb = g.pb;
@@ -1011,8 +1037,8 @@ __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *ac
             for (int m = 0; m < M; m++) dma_copy(dst + m * row, src + m * sstride, row);
         }
     }
-    if (P.in_parts && P.parts_lds)
-        dma_copy(act + M * cs * kActRec, reinterpret_cast<const uint8_t *>(P.in_parts), M * P.n_parts * 4);
+    if (P.parts && P.parts_lds)
+        dma_copy(act + M * cs * kActRec, reinterpret_cast<const uint8_t *>(P.parts), M * P.n_parts * 4);
     if (tr && lane == 0) tr[12] = now();
     // the transfers have written LDS once this wave's loads are complete
     __builtin_amdgcn_s_waitcnt(0);
@@ -1025,11 +1051,11 @@ __device__ __forceinline__ void stage(const PD &P, const UnitPos &g, uint8_t *ac
 // that depends only on the number of partials).  The partials come from LDS
 // where they were staged, else from global memory, a position's loads all
 // issued before the first add.
-template <int M, class PD>
-__device__ __forceinline__ void stage_rscale(const PD &P, const UnitPos &g, const uint8_t *act, Shared<M> &sh) {
+template <int M>
+__device__ __forceinline__ void stage_rscale(const StageIn &P, const UnitPos &g, const uint8_t *act, Shared<M> &sh) {
     const int lane = threadIdx.x & 63;
     const int K = P.K, n_parts = P.n_parts;
-    if (!P.in_parts) {
+    if (!P.parts) {
         if (lane < M) sh.rscale[lane] = 1.0f;
         return;
     }
@@ -1040,7 +1066,7 @@ __device__ __forceinline__ void stage_rscale(const PD &P, const UnitPos &g, cons
         if (P.parts_lds) {
             for (int i = lane; i < n_parts; i += 64) t += lp[m * n_parts + i];
         } else {
-            const float *gp = P.in_parts + m * n_parts;
+            const float *gp = P.parts + m * n_parts;
             float v[kPartsPerLane];
 #pragma unroll
             for (int k = 0; k < kPartsPerLane; k++) {
@@ -1351,13 +1377,14 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
                 }
             }
             bool fresh = false;
+            const StageIn si = stage_in(P);
             if (!inside) {
                 const unsigned *wt = P.wait;
                 if (wt && !wait_ready(wt, P.wait_target, status)) {
                     if (lane == 0) sh.abort = 1u;
                 } else {
                     if (tr && lane == 0) tr[1] = now();
-                    stage<M>(P, g, act, sh, tr);
+                    stage<M>(si, g, act, sh, tr);
                     if (tr && lane == 0) tr[2] = now();
                     st_q = aq;
                     st_parts = parts;
@@ -1372,7 +1399,7 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
             }
             lds_barrier();   // B1
             if (sh.abort) break;
-            if (fresh) stage_rscale<M>(P, g, act, sh);
+            if (fresh) stage_rscale<M>(si, g, act, sh);
         }
         const float g_cur = gamma_of(P, c.u);   // in flight while the unit computes
         lds_barrier();       // B2: the compute waves have written the unit's partial sums
