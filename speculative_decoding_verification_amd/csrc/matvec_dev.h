@@ -1119,7 +1119,12 @@ template <int M, class PD>
 __device__ __forceinline__ void store_y(const PD &P, int mt, int64_t row0, const TileVals<M> &x) {
     const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
     const int64_t N = P.N;
-    float *y = P.y[mt];
+    // integer arithmetic, not an index: an indexed pick from the three
+    // fields would put them in memory
+    const uint64_t m0 = mt == 0, m1 = mt == 1, m2 = mt == 2;
+    float *y = reinterpret_cast<float *>(m0 * reinterpret_cast<uint64_t>(P.y[0]) +
+                                         m1 * reinterpret_cast<uint64_t>(P.y[1]) +
+                                         m2 * reinterpret_cast<uint64_t>(P.y[2]));
     if (!y) return;
     const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), N - row0));
 #pragma unroll
@@ -1184,13 +1189,57 @@ __device__ __forceinline__ void finish_tile(const PD &P, int64_t row0, const Til
 // The norm weight of the epilogue for row lane & 31 of unit u's tile,
 // requested before the unit's barrier so it has arrived when the epilogue
 // runs (1 when there is none).
+// The phase fields a unit's finish reads, taken from the phase table while
+// the unit computes: the table is read through vector loads, and the
+// barrier before the finish orders memory, so a field first read after it
+// would put a memory round trip in front of the unit's stores.  The names
+// are the phase descriptor's, so the finish helpers take either.
+struct FinishIn {
+    int32_t N, n_w, fused, mu, S1, ep_mode, ep_src, count_all;
+    float *y[3];
+    const float *gamma;
+    int8_t *oq;
+    float *od;
+    int32_t *os16;
+    float *osumsq;
+    unsigned long long *argmax;
+    float *partial;
+    unsigned *tile_count;
+    unsigned *ready;
+};
 template <class PD>
-__device__ __forceinline__ float gamma_of(const PD &P, uint32_t u) {
+__device__ __forceinline__ FinishIn finish_in(const PD &P) {
+    FinishIn f;
+    f.N = P.N;
+    f.n_w = P.n_w;
+    f.fused = P.fused;
+    f.mu = P.mu;
+    f.S1 = P.S1;
+    f.ep_mode = P.ep_mode;
+    f.ep_src = P.ep_src;
+    f.count_all = P.count_all;
+    f.y[0] = P.y[0];
+    f.y[1] = P.y[1];
+    f.y[2] = P.y[2];
+    f.gamma = P.gamma;
+    f.oq = P.oq;
+    f.od = P.od;
+    f.os16 = P.os16;
+    f.osumsq = P.osumsq;
+    f.argmax = P.argmax;
+    f.partial = P.partial;
+    f.tile_count = P.tile_count;
+    f.ready = P.ready;
+    return f;
+}
+
+__device__ __forceinline__ float gamma_of(const FinishIn &P, const UnitPos &g) {
     const float *gamma = P.gamma;
     if (!gamma || P.ep_mode == SV_EP_NONE) return 1.0f;
-    const int64_t row = static_cast<int64_t>(unit_pos(P, u).tile) * kRows + (threadIdx.x & 31);
+    const int64_t row = static_cast<int64_t>(g.tile) * kRows + (threadIdx.x & 31);
     return row < P.N ? gld(gamma + row) : 1.0f;
 }
+
 
 // The control wave's part of a unit whose partial sums sit in wave-partial
 // buffer wp, right after the unit's barrier, in two halves.  finish_issue
@@ -1206,12 +1255,11 @@ __device__ __forceinline__ bool unit_split(const PD &P, const UnitPos &g) {
     return g.nch > 1 || (P.ep_mode == SV_EP_PAIR && !P.fused);
 }
 
-template <int M, class PD>
-__device__ __forceinline__ void finish_issue(const PD &P, uint32_t u, const float *wp, float g_row, Shared<M> &sh,
-                                             unsigned long long *tr) {
+template <int M>
+__device__ __forceinline__ void finish_issue(const FinishIn &P, const UnitPos &g, const float *wp, float g_row,
+                                             Shared<M> &sh, unsigned long long *tr) {
     if (tr && (threadIdx.x & 63) == 0) tr[7] = now();
     const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5, hr = r >> 4, rr = r & 15;
-    const UnitPos g = unit_pos(P, u);
     const int64_t row0 = static_cast<int64_t>(g.tile) * kRows;
     const int64_t N = P.N;
     const int nm = P.fused ? 2 : 1;
@@ -1265,11 +1313,10 @@ __device__ __forceinline__ void finish_issue(const PD &P, uint32_t u, const floa
     if (tr && lane == 0) tr[8] = now();
 }
 
-template <int M, class PD>
-__device__ __forceinline__ void finish_complete(const PD &P, uint32_t u, float g_row, Shared<M> &sh,
-                                                unsigned long long *tr) {
+template <int M>
+__device__ __forceinline__ void finish_complete(const FinishIn &P, const UnitPos &g, uint32_t u, float g_row,
+                                                Shared<M> &sh, unsigned long long *tr) {
     const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
-    const UnitPos g = unit_pos(P, u);
     const int64_t row0 = static_cast<int64_t>(g.tile) * kRows;
     const int64_t N = P.N;
     const bool pair = P.ep_mode == SV_EP_PAIR;
@@ -1401,13 +1448,14 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
             if (sh.abort) break;
             if (fresh) stage_rscale<M>(si, g, act, sh);
         }
-        const float g_cur = gamma_of(P, c.u);   // in flight while the unit computes
+        const FinishIn fi = finish_in(P);       // in flight while the unit computes
+        const float g_cur = gamma_of(fi, g);
         lds_barrier();       // B2: the compute waves have written the unit's partial sums
         if (sh.abort) break;
         unsigned long long *tf = n_units == 0 ? tr : nullptr;
         if (tf && lane == 0) tr[3] = now();
-        finish_issue<M>(P, c.u, wpart_buf<M>(smem, buf), g_cur, sh, tf);
-        finish_complete<M>(P, c.u, g_cur, sh, tf);
+        finish_issue<M>(fi, g, wpart_buf<M>(smem, buf), g_cur, sh, tf);
+        finish_complete<M>(fi, g, c.u, g_cur, sh, tf);
         if (tr && lane == 0) {
             if (tf) tr[4] = now();
             tr[5] = now();
