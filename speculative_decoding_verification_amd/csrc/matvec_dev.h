@@ -83,15 +83,22 @@ struct UnitCur {
     uint32_t i, end;   // the workgroup's schedule entries [i, end) (pass)
 };
 
+// Scalar: the phase and list indices are wave-uniform, so the table and the
+// lists can be read with scalar loads through the scalar cache.  That
+// shortens the per-unit table reads, which set the pace at one row (units
+// are short there); with more rows the same pass measured slower with
+// scalar reads, so they are taken at M = 1 only.
+template <bool Scalar>
 struct ManyTab {
     const SV_AS4 PhaseDesc *t;
     const SV_AS4 uint32_t *sched;   // [G + 1] entry offsets per workgroup, then the entries
     int n;
     uint32_t G;
-    __device__ __forceinline__ const SV_AS4 PhaseDesc &operator[](int p) const { return t[p]; }
+    static __device__ __forceinline__ int uni(int i) { return Scalar ? __builtin_amdgcn_readfirstlane(i) : i; }
+    __device__ __forceinline__ const SV_AS4 PhaseDesc &operator[](int p) const { return t[uni(p)]; }
     __device__ __forceinline__ void decode(UnitCur &c) const {
         if (c.i < c.end) {
-            const uint32_t e = sched[G + 1 + c.i];
+            const uint32_t e = sched[G + 1 + static_cast<uint32_t>(uni(static_cast<int>(c.i)))];
             c.p = static_cast<int>(e >> 20);
             c.u = e & 0xFFFFFu;
         } else {
@@ -1513,7 +1520,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
         if (threadIdx.x == 0) st_dev(ctl + kCtlArgmaxClear, 1u);
     }
     __syncthreads();
-    const ManyTab tab{reinterpret_cast<const SV_AS4 PhaseDesc *>(reinterpret_cast<uintptr_t>(table)),
+    const ManyTab<M == 1> tab{reinterpret_cast<const SV_AS4 PhaseDesc *>(reinterpret_cast<uintptr_t>(table)),
                       reinterpret_cast<const SV_AS4 uint32_t *>(reinterpret_cast<uintptr_t>(sched)), n_phases,
                       gridDim.x};
     if (threadIdx.x < kCompWaves * 64) compute_waves<M>(tab, n_phases, blockIdx.x, gridDim.x, smem, sh);
