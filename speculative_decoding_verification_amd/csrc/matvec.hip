@@ -472,54 +472,140 @@ static void host_unit_range(const PhaseDesc &P, uint32_t u, int &c0, int &c1, in
 // phase by phase, to the workgroup that can start it first, preferring one
 // that has its input chunk staged already.  Within a phase the units go out
 // last to first, so the finely cut units of a balanced phase run first and
-// each workgroup ends the phase on a unit whose tile needs no combine.  So a phase that
-// no later phase waits for fills the workgroups a narrower phase leaves
-// idle, instead of delaying the phase after it.  Each workgroup's list is
-// in phase order and every wait is for an earlier phase, so the launch
-// cannot deadlock whatever the model gets wrong; the model only decides
-// how well the work is spread.
+// each workgroup ends the phase on a unit whose tile needs no combine.
+// A phase that no phase waits for (no reader) is placed after the phase
+// that follows it: each of its units goes into a workgroup's idle gap
+// before that workgroup turns to the next phase (the time it would start
+// waiting for that phase's input, or the hand-off after that phase for a
+// workgroup with no unit in it), and only a unit that fits no gap delays
+// a later unit, where it delays least.  Its entries go in front of the next
+// phase's, so each workgroup's list stays in phase order and every wait is
+// for an earlier phase: the launch cannot deadlock whatever the model gets
+// wrong; the model only decides how well the work is spread.
 static void schedule(const std::vector<PhaseDesc> &host, const std::vector<int> &producer, int M, int G,
                      std::vector<uint32_t> &out) {
     const int n = static_cast<int>(host.size());
-    const double rate = 26000.0 / (1.0 + 0.09 * (M - 1));   // bytes per microsecond per workgroup
-    const double unit_ovh = 0.5, hand = 1.0, stage = 1.4 + 0.8 * (M - 1);
+    // per workgroup: streaming rate in bytes per microsecond, and the fixed
+    // costs of a unit, a hand-off and a staged chunk in microseconds
+    const double rate = 26000.0 / (1.0 + 0.13 * (M - 1));
+    const double unit_ovh = 0.5, hand = 1.0, stage = 1.1 + 0.18 * (M - 1);
+    std::vector<int> readers(n, 0);
+    for (int p = 0; p < n; p++)
+        if (producer[p] >= 0) readers[producer[p]]++;
     std::vector<double> free_at(G, 0.0), phase_end(n, 0.0);
-    std::vector<const void *> st_in(G, nullptr);
-    std::vector<int> st_b(G, -1), st_c(G, 0);
+    struct Staged {
+        const void *in = nullptr;
+        int b = -1, c = 0;
+    };
+    std::vector<Staged> st(G);
     std::vector<std::vector<uint32_t>> lists(G);
-    for (int p = 0; p < n; p++) {
-        const PhaseDesc &P = host[p];
-        const double ready = producer[p] >= 0 ? phase_end[producer[p]] + hand : 0.0;
+    auto ready_of = [&](int p) { return producer[p] >= 0 ? phase_end[producer[p]] + hand : 0.0; };
+    struct UnitModel {
+        double cost;
+        int sb, cs, pb, pcs;
+    };
+    auto model = [&](const PhaseDesc &P, uint32_t u) {
+        UnitModel m;
+        int c0, c1;
+        host_unit_range(P, u, c0, c1, m.sb, m.cs, m.pb, m.pcs);
         const double row_bytes = static_cast<double>(P.bbytes) / 16.0 * (P.fused ? 2.0 : 1.0);
+        m.cost = kRows * (c1 - c0) * row_bytes / rate + unit_ovh;
+        return m;
+    };
+    auto staged = [](const Staged &s, const PhaseDesc &P, const UnitModel &m) {
+        return s.in == P.aq && m.sb >= s.b && m.sb + m.cs <= s.b + s.c;
+    };
+    auto place = [&](int p) {
+        const PhaseDesc &P = host[p];
+        const double ready = ready_of(p);
         // the units of tiles cut finer than S chunks (the last ones) are
         // given out first: their partial sums are combined while the whole
         // units run, so a phase ends on units that need no combine
         for (int ui = P.n_units - 1; ui >= 0; ui--) {
-            const uint32_t u = static_cast<uint32_t>(ui);
-            int c0, c1, sb, cs, pb, pcs;
-            host_unit_range(P, u, c0, c1, sb, cs, pb, pcs);
-            const double cost = kRows * (c1 - c0) * row_bytes / rate + unit_ovh;
+            const UnitModel m = model(P, static_cast<uint32_t>(ui));
             int best = 0;
             double best_t = 1e300;
             bool best_staged = false;
             for (int w = 0; w < G; w++) {
-                const bool staged = st_in[w] == P.aq && sb >= st_b[w] && sb + cs <= st_b[w] + st_c[w];
-                const double t0 = std::max(free_at[w], ready) + (staged ? 0.0 : stage);
-                if (t0 < best_t - 1e-9) {
+                const bool sg = staged(st[w], P, m);
+                const double t0 = std::max(free_at[w], ready) + (sg ? 0.0 : stage);
+                // of equal starts, the workgroup idle longest: so a narrow
+                // phase does not land on the workgroups that ran the narrow
+                // phase before it, and the idle gaps alternate
+                if (t0 < best_t - 1e-9 || (t0 < best_t + 1e-9 && free_at[w] < free_at[best] - 1e-9)) {
                     best_t = t0;
                     best = w;
-                    best_staged = staged;
+                    best_staged = sg;
                 }
             }
-            if (!best_staged) {
-                st_in[best] = P.aq;
-                st_b[best] = pb;
-                st_c[best] = pcs;
-            }
-            free_at[best] = best_t + cost;
+            if (!best_staged) st[best] = {P.aq, m.pb, m.pcs};
+            free_at[best] = best_t + m.cost;
             phase_end[p] = std::max(phase_end[p], free_at[best]);
-            lists[best].push_back(static_cast<uint32_t>(p) << 20 | u);
+            lists[best].push_back(static_cast<uint32_t>(p) << 20 | static_cast<uint32_t>(ui));
         }
+    };
+    // the units of phase d (no reader) around phase p = d + 1, already placed
+    // from the state `gap`, `gst` (free times and staged chunks before p)
+    auto fill = [&](int d, int p, const std::vector<double> &gap, const std::vector<Staged> &gst,
+                    const std::vector<size_t> &mark) {
+        const PhaseDesc &D = host[d];
+        const double ready = ready_of(d), ready_p = ready_of(p);
+        std::vector<double> cur(gap), deadline(G);
+        std::vector<Staged> cst(gst);
+        std::vector<size_t> ins(G, 0);
+        std::vector<bool> has_p(G);
+        for (int w = 0; w < G; w++) {
+            has_p[w] = lists[w].size() > mark[w];
+            deadline[w] = has_p[w] ? std::max(gap[w], ready_p) : phase_end[p] + hand;
+        }
+        for (int ui = D.n_units - 1; ui >= 0; ui--) {
+            const UnitModel m = model(D, static_cast<uint32_t>(ui));
+            int best = 0;
+            double best_over = 1e300, best_t = 1e300;
+            bool best_staged = false;
+            for (int w = 0; w < G; w++) {
+                const bool sg = staged(cst[w], D, m);
+                const double t0 = std::max(cur[w], ready) + (sg ? 0.0 : stage);
+                const double over = std::max(0.0, t0 + m.cost - deadline[w]);
+                if (over < best_over - 1e-9 || (over < best_over + 1e-9 && t0 < best_t - 1e-9)) {
+                    best_over = over;
+                    best_t = t0;
+                    best = w;
+                    best_staged = sg;
+                }
+            }
+            if (!best_staged) cst[best] = {D.aq, m.pb, m.pcs};
+            cur[best] = best_t + m.cost;
+            phase_end[d] = std::max(phase_end[d], cur[best]);
+            lists[best].insert(lists[best].begin() + static_cast<std::ptrdiff_t>(mark[best] + ins[best]++),
+                               static_cast<uint32_t>(d) << 20 | static_cast<uint32_t>(ui));
+        }
+        // a workgroup whose gap overflowed runs its later units that much later
+        for (int w = 0; w < G; w++) {
+            if (!ins[w]) continue;
+            if (has_p[w]) {
+                const double over = std::max(0.0, cur[w] - deadline[w]);
+                free_at[w] += over;
+                phase_end[p] = std::max(phase_end[p], free_at[w]);
+            } else {
+                free_at[w] = std::max(free_at[w], cur[w]);
+                st[w] = cst[w];
+            }
+        }
+    };
+    for (int p = 0; p < n; p++) {
+        if (readers[p] == 0 && p + 1 < n) {
+            // phase p waits until phase p + 1 is placed
+            std::vector<double> gap(free_at);
+            std::vector<Staged> gst(st);
+            std::vector<size_t> mark(G);
+            for (int w = 0; w < G; w++) mark[w] = lists[w].size();
+            place(p + 1);
+            fill(p, p + 1, gap, gst, mark);
+            p++;
+            continue;
+        }
+        place(p);
     }
     out.assign(static_cast<size_t>(G) + 1, 0u);
     for (int w = 0; w < G; w++) out[w + 1] = out[w] + static_cast<uint32_t>(lists[w].size());
