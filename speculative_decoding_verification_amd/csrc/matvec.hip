@@ -78,15 +78,17 @@ static int resident_per_cu(int M, size_t lds, const hipDeviceProp_t &prop, int o
 }
 
 constexpr size_t kDefaultLds = 64 * 1024;
+constexpr size_t kStaticLds = 1024;   // held for the kernels' own __shared__ variables (224 bytes today)
 
-// Largest dynamic LDS one workgroup may use on the current device.
+// Largest dynamic LDS one workgroup may use on the current device: the
+// device's LDS per workgroup less what the kernels declare statically.
 static int lds_limit(size_t *limit) {
     int dev = 0;
     hipDeviceProp_t prop;
     int rc = hip_check(hipGetDevice(&dev), "device query");
     if (!rc) rc = hip_check(hipGetDeviceProperties(&prop, dev), "device query");
     if (rc) return rc;
-    *limit = std::max(static_cast<size_t>(prop.sharedMemPerBlock), kDefaultLds);
+    *limit = std::max(static_cast<size_t>(prop.sharedMemPerBlock) - kStaticLds, kDefaultLds);
     return SV_OK;
 }
 
@@ -162,24 +164,26 @@ static size_t parts_bytes(const PhaseDesc &P, int M) {
 }
 
 static size_t phase_lds(const PhaseDesc &P, int M) {
-    return static_cast<size_t>(M) * P.chunk_sub * kActRec + (P.parts_lds ? parts_bytes(P, M) : 0);
+    return static_cast<size_t>(M) * row_sub_of(M, P.chunk_sub) * kActRec + (P.parts_lds ? parts_bytes(P, M) : 0);
 }
 
-// Stages the RMS partials of every phase into LDS when the launch's LDS
+// Stages the RMS partials of a phase's input into LDS when the phase's LDS
 // still fits the device with them (the factors are then formed from LDS
-// right after the staging wait); otherwise the factors read them from
-// global memory.  The sum is the same either way.
+// right after the staging wait); otherwise that phase's factors read them
+// from global memory.  The sum is the same either way.
 static int place_parts(PhaseDesc *P, int n, int M) {
-    size_t with = 0;
-    for (int i = 0; i < n; i++)
-        with = std::max(with, static_cast<size_t>(M) * P[i].chunk_sub * kActRec + parts_bytes(P[i], M));
-    with += wpart_bytes(M);
-    size_t limit = kDefaultLds;
-    if (with > kDefaultLds) {
-        const int rc = lds_limit(&limit);
-        if (rc) return rc;
+    size_t limit = 0;
+    bool queried = false;
+    for (int i = 0; i < n; i++) {
+        const size_t with =
+            static_cast<size_t>(M) * row_sub_of(M, P[i].chunk_sub) * kActRec + parts_bytes(P[i], M) + wpart_bytes(M);
+        if (with > kDefaultLds && !queried) {
+            const int rc = lds_limit(&limit);
+            if (rc) return rc;
+            queried = true;
+        }
+        P[i].parts_lds = P[i].in_parts && (with <= kDefaultLds || with <= limit) ? 1 : 0;
     }
-    for (int i = 0; i < n; i++) P[i].parts_lds = P[i].in_parts && with <= limit ? 1 : 0;
     return SV_OK;
 }
 

@@ -399,33 +399,38 @@ __device__ __forceinline__ float block_term(const WDec &w, const ARec &a, const 
     }
 }
 
-// LDS layout of a staged chunk of cs sub-blocks of all M positions: codes
-// [M][cs][32] (the global bytes as they are), scales [M][cs] fp32, code sums
-// [M][cs][2] int32; where they are staged, the RMS partials of the input
-// follow, [M][n_parts].
+// LDS layout of a staged chunk of cs sub-blocks of all M positions, with
+// R = row_sub<M>(cs) (kRowSub, or cs at M = 1): codes [M][R][32] (the global
+// bytes as they are), scales [M][R] fp32, code sums [M][R][2] int32, each
+// position's row holding the chunk's cs records first; where they are
+// staged, the RMS partials of the input follow, [M][n_parts].
 struct ActLds {
     const uint8_t *q;
     const float *d;
     const int2 *x;
-    int cs, begin;   // staged sub-blocks [begin, begin + cs) of K
+    int begin;   // first staged sub-block of K
 };
-__device__ __forceinline__ ActLds act_lds(const uint8_t *act, int M, int cs, int begin) {
+template <int M>
+__device__ __forceinline__ ActLds act_lds(const uint8_t *act, int cs, int begin) {
     ActLds a;
     a.begin = begin;
     a.q = act;
-    a.d = reinterpret_cast<const float *>(act + M * cs * 32);
-    a.x = reinterpret_cast<const int2 *>(act + M * cs * 36);
-    a.cs = cs;
+    a.d = reinterpret_cast<const float *>(act + M * row_sub<M>(cs) * 32);
+    a.x = reinterpret_cast<const int2 *>(act + M * row_sub<M>(cs) * 36);
     return a;
 }
+// With several positions, every position's row of a field starts kRowSub
+// records after the previous one whatever the chunk's length, so a
+// position's offset is a constant of the instruction and only the
+// sub-block's address is computed.
 __device__ __forceinline__ void read_act(ARec &r, const ActLds &A, int m, int sl) {
-    const uint8_t *q = A.q + (m * A.cs + sl) * 32;
+    const uint8_t *q = A.q + (m * kRowSub + sl) * 32;
     const uint4 lo = *reinterpret_cast<const uint4 *>(q);
     const uint4 hi = *reinterpret_cast<const uint4 *>(q + 16);
     r.v[0] = lo.x; r.v[1] = lo.y; r.v[2] = lo.z; r.v[3] = lo.w;
     r.v[4] = hi.x; r.v[5] = hi.y; r.v[6] = hi.z; r.v[7] = hi.w;
-    r.d = A.d[m * A.cs + sl];
-    const int2 x = A.x[m * A.cs + sl];
+    r.d = A.d[m * kRowSub + sl];
+    const int2 x = A.x[m * kRowSub + sl];
     r.x0 = x.x;
     r.x1 = x.y;
 }
@@ -858,7 +863,7 @@ __device__ __forceinline__ void ring_step(const Tab &tab, int n_phases, uint32_t
         } else {
             st.stb = sh.stb;
             st.stc = sh.stc;
-            st.A = act_lds(act_base<M>(smem), M, st.stc, st.stb);
+            st.A = act_lds<M>(act_base<M>(smem), st.stc, st.stb);
         }
     }
     if (st.go) consume<M>(s, st.C, st.A, st.acc);
@@ -1027,25 +1032,28 @@ __device__ __forceinline__ void stage(const StageIn &P, const UnitPos &g, uint8_
     const int K = P.K, nsub = K >> 5, cs = g.pcs, sb = g.pb;
     // the unit's chunk of S (which holds the unit's own range); three
     // fields, each M rows: codes (row stride K), scales (nsub floats),
-    // code sums (K / 16 ints); the LDS rows are contiguous, field after field
+    // code sums (K / 16 ints); in LDS each field's rows are row_sub records
+    // apart, field after field
 #pragma unroll 1
     for (int f = 0; f < 3; f++) {
+        const int rec = f == 0 ? 32 : (f == 1 ? 4 : 8);
         const uint8_t *src = f == 0 ? reinterpret_cast<const uint8_t *>(P.aq) + static_cast<int64_t>(sb) * 32
                              : f == 1 ? reinterpret_cast<const uint8_t *>(P.ad + sb)
                                       : reinterpret_cast<const uint8_t *>(P.as16 + 2 * sb);
         const int64_t sstride = f == 0 ? K : (f == 1 ? nsub * 4 : (K >> 4) * 4);
-        const int row = f == 0 ? cs * 32 : (f == 1 ? cs * 4 : cs * 8);
-        uint8_t *dst = act + (f == 0 ? 0 : (f == 1 ? M * cs * 32 : M * cs * 36));
-        if (sstride == row) {
-            // the chunk is the whole row: the M rows are contiguous in memory
+        const int row = cs * rec, lrow = row_sub<M>(cs) * rec;
+        uint8_t *dst = act + (f == 0 ? 0 : (f == 1 ? M * row_sub<M>(cs) * 32 : M * row_sub<M>(cs) * 36));
+        if (sstride == row && row == lrow) {
+            // the chunk is the whole row and fills the LDS row: the M rows
+            // are contiguous in both
             dma_copy(dst, src, M * row);
         } else {
 #pragma unroll 1
-            for (int m = 0; m < M; m++) dma_copy(dst + m * row, src + m * sstride, row);
+            for (int m = 0; m < M; m++) dma_copy(dst + m * lrow, src + m * sstride, row);
         }
     }
     if (P.parts && P.parts_lds)
-        dma_copy(act + M * cs * kActRec, reinterpret_cast<const uint8_t *>(P.parts), M * P.n_parts * 4);
+        dma_copy(act + M * row_sub<M>(cs) * kActRec, reinterpret_cast<const uint8_t *>(P.parts), M * P.n_parts * 4);
     if (tr && lane == 0) tr[12] = now();
     // the transfers have written LDS once this wave's loads are complete
     __builtin_amdgcn_s_waitcnt(0);
@@ -1066,7 +1074,7 @@ __device__ __forceinline__ void stage_rscale(const StageIn &P, const UnitPos &g,
         if (lane < M) sh.rscale[lane] = 1.0f;
         return;
     }
-    const float *lp = reinterpret_cast<const float *>(act + M * g.pcs * kActRec);
+    const float *lp = reinterpret_cast<const float *>(act + M * row_sub<M>(g.pcs) * kActRec);
 #pragma unroll 1
     for (int m = 0; m < M; m++) {
         float t = 0.0f;

@@ -12,6 +12,13 @@ constexpr int kThreads = 576;          // eight compute waves and one control wa
 constexpr int kRows = 32;              // rows per tile: 2 half tiles of 8 groups x 2 rows
 constexpr int kActRec = 32 + 4 + 8;    // LDS bytes per position per staged sub-block (codes, scale, sums)
 constexpr int kMaxChunkSteps = 20;     // most 256-element steps of K one unit covers
+constexpr int kRowSub = kMaxChunkSteps * 8;   // LDS row of a staged field: the largest chunk, in sub-blocks
+// Records from one position's row of a staged field to the next: kRowSub
+// with several positions (a position's offset is then a constant of the
+// instruction), the chunk itself with one (there is no second row).
+template <int M>
+__host__ __device__ constexpr int row_sub(int cs) { return M == 1 ? cs : kRowSub; }
+inline int row_sub_of(int M, int cs) { return M == 1 ? cs : kRowSub; }
 constexpr int kMaxS = 8;               // most K chunks of a tile (K <= 40960)
 constexpr int kBalanceGrid = 256;      // workgroups a balanced phase is cut for (one per CU)
 constexpr unsigned kSpinLimit = 1u << 22;
