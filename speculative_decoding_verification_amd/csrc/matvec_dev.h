@@ -996,6 +996,68 @@ __device__ __forceinline__ void dma_copy(uint8_t *dst, const uint8_t *src, int n
     }
 }
 
+// Copies M rows of `row` bytes, row m from src + m * sstride, into LDS rows
+// LROW bytes apart (dst + m * LROW), in one loop over the LDS span
+// (M - 1) LROW + row with 16-byte transfers; the caller checks that the
+// addresses, the stride and the row are multiples of 16.  A lane whose piece
+// falls in the tail of an LDS row, past its `row` bytes, loads the first
+// piece of the field again (a valid address) into that tail, which nothing
+// reads.  One loop instead of one copy per row: the per-copy set-up and the
+// partial transfer that ends every copy are paid once.
+template <int LROW>
+__device__ __forceinline__ void dma_rows(uint8_t *dst, const uint8_t *src, int sstride, int row, int M) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t rowu = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(row));
+    const uint32_t ssu = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(sstride));
+    const int span = __builtin_amdgcn_readfirstlane((M - 1) * LROW + row);
+    const uint32_t d0 = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>((uint32_t)(uintptr_t)(SV_AS3 uint8_t *)dst)));
+    const uint64_t sa = reinterpret_cast<uint64_t>(src);
+    const uint32_t slo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sa & 0xFFFFFFFFu)));
+    const uint32_t shi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sa >> 32)));
+    const uint64_t s0 = static_cast<uint64_t>(slo) | (static_cast<uint64_t>(shi) << 32);
+    const int full = span >> 10;                 // 1 KiB per whole-wave transfer
+    const int rest = (span >> 4) - (full << 6);  // 16-byte pieces after them
+    uint32_t o = lane * 16u;                     // the lane's LDS offset in the span
+#pragma unroll 1
+    for (int k = 0; k < full; k++) {
+        const uint32_t m = o / LROW, off = o - m * LROW;
+        const uint64_t a = s0 + (off < rowu ? m * ssu + off : 0u);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(a),
+                                         (SV_AS3 void *)static_cast<uintptr_t>(d0 + (k << 10)), 16, 0, 0);
+        o += 1024u;
+    }
+    if (rest > 0 && static_cast<int>(lane) < rest) {
+        const uint32_t m = o / LROW, off = o - m * LROW;
+        const uint64_t a = s0 + (off < rowu ? m * ssu + off : 0u);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(a),
+                                         (SV_AS3 void *)static_cast<uintptr_t>(d0 + (full << 10)), 16, 0, 0);
+    }
+}
+
+// One field of the staged chunk: M rows of cs records of REC bytes, row m
+// of the source at src + m * sstride, into LDS rows row_sub records apart.
+template <int M, int REC>
+__device__ __forceinline__ void stage_field(uint8_t *dst, const uint8_t *src, int sstride, int cs) {
+    const int row = cs * REC, lrow = row_sub<M>(cs) * REC;
+    if (sstride == row && row == lrow) {
+        // the chunk is the whole row and fills the LDS row: the M rows are
+        // contiguous in both
+        dma_copy(dst, src, M * row);
+        return;
+    }
+    if constexpr (M > 1) {
+        const uint64_t al = reinterpret_cast<uint64_t>(src) | static_cast<uint64_t>(sstride) |
+                            static_cast<uint64_t>(row) | static_cast<uint64_t>((uint32_t)(uintptr_t)(SV_AS3 uint8_t *)dst);
+        if ((__builtin_amdgcn_readfirstlane(static_cast<int>(al & 15u))) == 0) {
+            dma_rows<kRowSub * REC>(dst, src, sstride, row, M);
+            return;
+        }
+    }
+#pragma unroll 1
+    for (int m = 0; m < M; m++) dma_copy(dst + m * lrow, src + static_cast<int64_t>(m) * sstride, row);
+}
+
 // The phase fields that staging and the RMS factors read, taken from the
 // phase table before the wait for the input: the table is read through
 // vector loads, and one issued after the wait would put a memory round trip
@@ -1034,24 +1096,10 @@ __device__ __forceinline__ void stage(const StageIn &P, const UnitPos &g, uint8_
     // fields, each M rows: codes (row stride K), scales (nsub floats),
     // code sums (K / 16 ints); in LDS each field's rows are row_sub records
     // apart, field after field
-#pragma unroll 1
-    for (int f = 0; f < 3; f++) {
-        const int rec = f == 0 ? 32 : (f == 1 ? 4 : 8);
-        const uint8_t *src = f == 0 ? reinterpret_cast<const uint8_t *>(P.aq) + static_cast<int64_t>(sb) * 32
-                             : f == 1 ? reinterpret_cast<const uint8_t *>(P.ad + sb)
-                                      : reinterpret_cast<const uint8_t *>(P.as16 + 2 * sb);
-        const int64_t sstride = f == 0 ? K : (f == 1 ? nsub * 4 : (K >> 4) * 4);
-        const int row = cs * rec, lrow = row_sub<M>(cs) * rec;
-        uint8_t *dst = act + (f == 0 ? 0 : (f == 1 ? M * row_sub<M>(cs) * 32 : M * row_sub<M>(cs) * 36));
-        if (sstride == row && row == lrow) {
-            // the chunk is the whole row and fills the LDS row: the M rows
-            // are contiguous in both
-            dma_copy(dst, src, M * row);
-        } else {
-#pragma unroll 1
-            for (int m = 0; m < M; m++) dma_copy(dst + m * lrow, src + m * sstride, row);
-        }
-    }
+    const int rs = row_sub<M>(cs);
+    stage_field<M, 32>(act, reinterpret_cast<const uint8_t *>(P.aq) + static_cast<int64_t>(sb) * 32, K, cs);
+    stage_field<M, 4>(act + M * rs * 32, reinterpret_cast<const uint8_t *>(P.ad + sb), nsub * 4, cs);
+    stage_field<M, 8>(act + M * rs * 36, reinterpret_cast<const uint8_t *>(P.as16 + 2 * sb), (K >> 4) * 4, cs);
     if (P.parts && P.parts_lds)
         dma_copy(act + M * row_sub<M>(cs) * kActRec, reinterpret_cast<const uint8_t *>(P.parts), M * P.n_parts * 4);
     if (tr && lane == 0) tr[12] = now();
