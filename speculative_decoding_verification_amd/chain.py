@@ -158,9 +158,14 @@ class VerifyStack:
             self.acts.append({"in": _Act(M, H), "v": _Act(M, H), "o": _Act(M, H), "h": _Act(M, F)})
         self.a_final = _Act(M, H)
         self.a_in = self.acts[0]["in"]
-        self.yq = t.empty((M, H), dtype=t.float32, device="cuda")
-        self.yk = t.empty((M, H), dtype=t.float32, device="cuda")
-        self.yv = t.empty((M, H), dtype=t.float32, device="cuda")
+        # Each layer writes its q, k and v outputs to buffers of its own: a
+        # pass does not order two phases' writes to one y buffer, and a
+        # layer's q/k units fill idle workgroups wherever the schedule finds
+        # them, so a buffer shared by the layers could end with an earlier
+        # layer's rows.  yq, yk and yv are the last layer's.
+        self.ys = [{n: t.empty((M, H), dtype=t.float32, device="cuda") for n in "qkv"}
+                   for _ in range(max(shape.layers, 1))]
+        self.yq, self.yk, self.yv = self.ys[-1]["q"], self.ys[-1]["k"], self.ys[-1]["v"]
         self.logits = t.empty((M, shape.vocab or 1), dtype=t.float32, device="cuda")
         self.argmax = t.zeros((M,), dtype=t.int64, device="cuda")
         self.drafts = t.zeros((max(M - 1, 1),), dtype=t.int32, device="cuda")
@@ -176,18 +181,19 @@ class VerifyStack:
         for li, lw in enumerate(L):
             m = lw.mats
             a = self.acts[li]
+            y = self.ys[li]
             last = li + 1 == len(L)
             nxt = self.gamma_f if last else L[li + 1].gammas["g1"]
             out = self.a_final if last else self.acts[li + 1]["in"]
             if self.shape.attn_q == self.shape.v_q:
                 specs.append(("qkv", [m["q"][0], m["k"][0], m["v"][0]], a["in"].desc(M, eps),
-                              [self.yq, self.yk, self.yv], a["v"].ep(SV_EP_QUANT, lw.gammas["g2"], src=2)))
+                              [y["q"], y["k"], y["v"]], a["v"].ep(SV_EP_QUANT, lw.gammas["g2"], src=2)))
             else:
                 # v (its own format) first: o waits for it alone; q and k
                 # read the same input and have no reader
-                specs.append(("v", [m["v"][0]], a["in"].desc(M, eps), [self.yv],
+                specs.append(("v", [m["v"][0]], a["in"].desc(M, eps), [y["v"]],
                               a["v"].ep(SV_EP_QUANT, lw.gammas["g2"], src=0)))
-                specs.append(("qk", [m["q"][0], m["k"][0]], a["in"].desc(M, eps), [self.yq, self.yk], None))
+                specs.append(("qk", [m["q"][0], m["k"][0]], a["in"].desc(M, eps), [y["q"], y["k"]], None))
             specs.append(("o", [m["o"][0]], a["v"].desc(M, eps), [None],
                           a["o"].ep(SV_EP_QUANT, lw.gammas["g3"])))
             specs.append(("gate_up", [m["gate"][0], m["up"][0]], a["o"].desc(M, eps), [None, None],
