@@ -115,12 +115,16 @@ struct ManyTab {
         decode(c);
     }
 };
+// The single call's one phase, read where the launch argument lies (the
+// kernel argument segment, through scalar loads): a copy in the kernel would
+// be addressed by runtime indices (the matrix of a unit) and so live in
+// scratch memory.
 struct OneTab {
-    PhaseDesc P;
-    __device__ __forceinline__ const PhaseDesc &operator[](int) const { return P; }
+    const SV_AS4 PhaseDesc *t;
+    __device__ __forceinline__ const SV_AS4 PhaseDesc &operator[](int) const { return *t; }
     __device__ __forceinline__ void first(uint32_t b, UnitCur &c) const {
         c.u = b;
-        c.p = b < static_cast<uint32_t>(P.n_units) ? 0 : 1;
+        c.p = b < static_cast<uint32_t>(t->n_units) ? 0 : 1;
     }
     __device__ __forceinline__ void next(UnitCur &c) const { c.p = 1; }   // one unit per workgroup
 };
@@ -1544,7 +1548,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))
     if (threadIdx.x < SV_MAX_M) sh.best[threadIdx.x] = 0ull;
     if (threadIdx.x == 0) sh.abort = 0u;
     __syncthreads();
-    const OneTab tab{P};
+    // P is the launch's only argument, so it starts the argument segment
+    (void)P;
+    const OneTab tab{reinterpret_cast<const SV_AS4 PhaseDesc *>(
+        reinterpret_cast<uintptr_t>(__builtin_amdgcn_kernarg_segment_ptr()))};
     if (threadIdx.x < kCompWaves * 64) compute_waves<M>(tab, 1, blockIdx.x, gridDim.x, smem, sh);
     else control_wave<M>(tab, 1, blockIdx.x, gridDim.x, smem, sh, nullptr, nullptr, nullptr);
 }
