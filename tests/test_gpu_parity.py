@@ -126,7 +126,9 @@ def _encode_unit(qt, w):
 
 
 # ------------------------------------------------------------------ a3 tolerance parity
-SHAPES = [(96, 1024), (64, 2560), (160, 5120), (32, 768), (64, 9728), (32, 17408)]
+# K = 1056 and 5152 (Q8_0 only): K chunks whose scale and code-sum rows are
+# not whole 16-byte pieces (33 and 81 sub-blocks), staged row by row
+SHAPES = [(96, 1024), (64, 2560), (160, 5120), (32, 768), (64, 9728), (32, 17408), (64, 1056), (32, 5152)]
 
 
 @pytest.mark.parametrize("qt", QT)
