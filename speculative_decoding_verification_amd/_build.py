@@ -61,14 +61,16 @@ def _compile(job, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), link_extra=()) -> str:
+    """extra: more compile flags; link_extra: more link flags (a host-side
+    sanitizer build passes its runtime here)."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
     tmp = OUT + f".tmp{os.getpid()}"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
