@@ -237,6 +237,19 @@ typedef struct sv_pass sv_pass; /* opaque host handle */
  * phase is invalid (sv_last_error() says why). */
 size_t sv_pass_workspace_bytes(const sv_phase *phases, int32_t n_phases);
 
+/* Host only, no device call: the unit lists a pass over these phases runs
+ * with `grid` workgroups (1..1024), built as sv_pass_create builds them
+ * (the same validation, phase links and schedule), for inspecting how the
+ * phases of a cycle ("Inside OpenJet Engine: making speculative decoding
+ * pay", section "One GPU launch for a speculative cycle") are spread over
+ * the workgroups.  The buffers of `phases` are only compared as addresses,
+ * never read.  out (host, may be NULL) receives grid + 1 list offsets, then
+ * the entries, each (phase << 20) | unit, workgroup w's list being entries
+ * [offset[w], offset[w + 1]) in the order it runs them.  Returns the number
+ * of 32-bit words (grid + 1 + total units), or 0 with sv_last_error() set
+ * if a phase is invalid, grid is out of range or cap is below that number. */
+size_t sv_pass_schedule(const sv_phase *phases, int32_t n_phases, int32_t grid, uint32_t *out, size_t cap);
+
 /* Validates every phase (same M for all; buffers as below), writes the
  * phase table into `workspace` (device, 256-byte aligned,
  * sv_pass_workspace_bytes bytes; it must stay allocated and untouched while

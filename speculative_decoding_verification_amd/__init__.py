@@ -24,9 +24,10 @@ MAX_M = 16
 EXPORTS = [
     "sv_last_error", "sv_version", "sv_repacked_bytes", "sv_repack_weights", "sv_unpack_weights",
     "sv_quantize_act_q8", "sv_matvec_workspace_bytes", "sv_verify_matvec", "sv_head_workspace_bytes",
-    "sv_head_logits", "sv_argmax_index", "sv_pass_workspace_bytes", "sv_pass_create", "sv_pass_run",
-    "sv_pass_status", "sv_pass_trace", "sv_pass_destroy", "sv_accept_greedy", "sv_accept_workspace_bytes",
-    "sv_accept_rejection", "sv_accept_noalloc_max_bytes", "sv_accept_rejection_noalloc", "sv_read_bandwidth",
+    "sv_head_logits", "sv_argmax_index", "sv_pass_workspace_bytes", "sv_pass_schedule", "sv_pass_create",
+    "sv_pass_run", "sv_pass_status", "sv_pass_trace", "sv_pass_destroy", "sv_accept_greedy",
+    "sv_accept_workspace_bytes", "sv_accept_rejection", "sv_accept_noalloc_max_bytes",
+    "sv_accept_rejection_noalloc", "sv_read_bandwidth",
 ]
 
 
@@ -89,6 +90,8 @@ def lib():
                                      ctypes.c_size_t, P]
         L.sv_pass_workspace_bytes.restype = ctypes.c_size_t
         L.sv_pass_workspace_bytes.argtypes = [ctypes.POINTER(Phase), i32]
+        L.sv_pass_schedule.restype = ctypes.c_size_t
+        L.sv_pass_schedule.argtypes = [ctypes.POINTER(Phase), i32, i32, ctypes.c_void_p, ctypes.c_size_t]
         L.sv_pass_create.argtypes = [ctypes.POINTER(Phase), i32, P, ctypes.c_size_t, ctypes.POINTER(P)]
         L.sv_pass_run.argtypes = [P, P]
         L.sv_pass_status.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
@@ -240,6 +243,23 @@ def phase(weights, A: Act, ys=(), ep: Epilogue | None = None, row_ids=None, n_ro
     ph.n_rows = int(n_rows if row_ids is not None else 0)
     ph.argmax = None if argmax is None else argmax.data_ptr()
     return ph
+
+
+def pass_schedule(phases, grid: int):
+    """The unit lists a pass over `phases` runs with `grid` workgroups (host
+    only): (offsets [grid + 1], entries) as uint32 arrays, each entry
+    (phase << 20) | unit."""
+    import numpy as np
+    n = len(phases)
+    arr = (Phase * n)(*phases)
+    need = lib().sv_pass_schedule(arr, n, int(grid), None, 0)
+    if need == 0:
+        raise SpecVerifyError(SV_ERR_ARG, lib().sv_last_error().decode())
+    out = np.zeros(need, np.uint32)
+    got = lib().sv_pass_schedule(arr, n, int(grid), out.ctypes.data_as(ctypes.c_void_p), need)
+    if got != need:
+        raise SpecVerifyError(SV_ERR_ARG, lib().sv_last_error().decode())
+    return out[:grid + 1].copy(), out[grid + 1:].copy()
 
 
 class Pass:

@@ -727,6 +727,36 @@ extern "C" size_t sv_pass_workspace_bytes(const sv_phase *phases, int32_t n_phas
     return L.total;
 }
 
+extern "C" size_t sv_pass_schedule(const sv_phase *phases, int32_t n_phases, int32_t grid, uint32_t *out,
+                                   size_t cap) {
+    using namespace sv;
+    std::vector<PhaseDesc> host;
+    PassLayout L;
+    if (plan_pass(phases, n_phases, host, L) != SV_OK) return 0;
+    if (grid < 1 || grid > kMaxGrid) {
+        fail(SV_ERR_ARG, "pass_schedule: grid must be in [1, " + std::to_string(kMaxGrid) + "]");
+        return 0;
+    }
+    const int M = phases[0].A.M;
+    std::vector<int> producer;
+    if (link_phases(host, M, producer) != SV_OK) return 0;
+    std::vector<uint32_t> plan;
+    schedule(host, producer, M, grid, plan);
+    if (!schedule_ok(host, grid, plan)) {
+        fail(SV_ERR_ARG, "pass_schedule: internal error: inconsistent schedule");
+        return 0;
+    }
+    if (out) {
+        if (cap < plan.size()) {
+            fail(SV_ERR_ARG, "pass_schedule: out holds " + std::to_string(cap) + " words, the lists need " +
+                                 std::to_string(plan.size()));
+            return 0;
+        }
+        std::copy(plan.begin(), plan.end(), out);
+    }
+    return plan.size();
+}
+
 extern "C" int sv_pass_create(const sv_phase *phases, int32_t n_phases, void *workspace, size_t ws_bytes,
                               sv_pass **out) {
     using namespace sv;

@@ -4,7 +4,8 @@
 #  2. the C-ABI library's host code (every hipcc compile and the link get
 #     -Xarch_host -fsanitize=...; the gfx950 device code is built as usual)
 #     under the ABI host tests (argument checks, workspace sizes, error
-#     paths and the allocation-free entry point's limits).
+#     paths, the allocation-free entry point's limits) and the host tests of
+#     pass planning (phase links and the schedule of whole stacks).
 # Everything is built in a scratch copy of the sources (SV_SAN_DIR, default
 # /tmp/sv_sanitize), so the in-tree builds are untouched.  gcc's and clang's
 # sanitizer runtimes cannot share a process, so the two parts run in
@@ -26,7 +27,7 @@ gcc -O1 -g -std=c11 -ffp-contract=off -fno-fast-math -fsanitize=address,undefine
     -fno-omit-frame-pointer -fPIC -shared -pthread -o oracle/liboracle.so oracle/oracle.c -lm
 GCC_RT="$(gcc -print-file-name=libasan.so):$(gcc -print-file-name=libubsan.so)"
 LD_PRELOAD="$GCC_RT${PRE:+:$PRE}" python -m pytest tests -q -m "not gpu" -p no:cacheprovider \
-    --deselect tests/test_abi_host.py
+    --deselect tests/test_abi_host.py --deselect tests/test_schedule_host.py
 
 echo "== library host code with clang ASan + UBSan"
 python - <<'PY'
@@ -43,5 +44,6 @@ PY
 # the oracle again without sanitizers: gcc's runtime is not in this process
 python -c "import sys; sys.path.insert(0, '.'); import oracle; oracle.build(force=True)"
 CLANG_RT=$(ls /opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so | head -1)
-LD_PRELOAD="$CLANG_RT${PRE:+:$PRE}" python -m pytest tests/test_abi_host.py -q -p no:cacheprovider
+LD_PRELOAD="$CLANG_RT${PRE:+:$PRE}" python -m pytest tests/test_abi_host.py tests/test_schedule_host.py -q \
+    -p no:cacheprovider
 echo "sanitizer runs passed"
