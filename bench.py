@@ -218,8 +218,11 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     return nbytes
 
 
+# the pass kernel and what decides its work: the decomposition and the
+# schedule of units (matvec.hip) set which units run where and how often an
+# input is staged, so they change a launch's traffic as much as its code does
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decoding_verification_amd", "csrc", f)
-                  for f in ("matvec_dev.h", "matvec_launch.h", "matvec_inst.hip", "sv_internal.h")]
+                  for f in ("matvec_dev.h", "matvec_launch.h", "matvec_inst.hip", "sv_internal.h", "matvec.hip")]
 
 
 def traffic_file(config, M):
