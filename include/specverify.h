@@ -288,17 +288,23 @@ int sv_pass_run(const sv_pass *pass, void *stream);
 int sv_pass_status(const sv_pass *pass, uint32_t *status);
 
 /* Profiling.  enable != 0 makes later runs record, per workgroup and phase,
- * twelve words: the 100 MHz real-time counter when the workgroup reached
- * the phase, when its input became ready, when its first unit had staged
- * the input, finished its dot products, and was done (outputs written and
- * counted), when its last unit was done, the number of units it ran, when
- * the first unit had its output rows combined and when its epilogue was
- * written (0 if that unit did not run the epilogue), the workgroup's
- * placement (the HW_ID register in the low 32 bits, XCC_ID in the high 32),
- * and two unused words ([grid][n_phases][12], zero rows for phases in which
- * a workgroup had no unit).  With host != NULL the last run's record is
- * copied there (synchronous; bytes >= grid * n_phases * 96).  *grid (may be
- * NULL) receives the number of workgroups a run launches. */
+ * sixteen 64-bit words, [grid][n_phases][16], zero rows for phases in which
+ * a workgroup had no unit.  Times are the 100 MHz real-time counter:
+ *   0 the workgroup reached the phase;  1 its input was ready;  2 the input
+ *   was staged;  3 the first unit's dot products were done (its partial sums
+ *   handed to the control wave);  4 the first unit was done (outputs written
+ *   and counted);  5 the last unit was done;  6 the number of units it ran;
+ *   7 the first unit's rows were combined;  8 its outputs or partial sums
+ *   were written;  9 the workgroup's placement (the HW_ID register in the
+ *   low 32 bits, XCC_ID in the high 32);  10 the first unit's partial sums
+ *   had landed (a tile split over K; else 0);  11 its outputs had landed,
+ *   before the hand-off count (0 if no later phase reads it);  12 the
+ *   staging transfers were issued;  13 they had landed;  14, 15 unused.
+ * Words 1, 2, 12 and 13 describe the workgroup's last staging in the
+ * phase (most phases stage once per workgroup).  With host != NULL the last
+ * run's record is copied there (synchronous; bytes >= grid * n_phases *
+ * 128).  *grid (may be NULL) receives the number of workgroups a run
+ * launches. */
 int sv_pass_trace(sv_pass *pass, int enable, uint64_t *host, size_t bytes, int32_t *grid);
 
 void sv_pass_destroy(sv_pass *pass);

@@ -540,10 +540,12 @@ __device__ __forceinline__ uint8_t *act_base(uint8_t *smem) {
     return smem + 2 * kCompWaves * NMat<M>::value * M * 16 * 4;
 }
 
-// Trace record of a (workgroup, phase) (control wave): real-time counter at
-// the first unit of the phase, input ready, input staged, first unit
-// computed, first unit handed off, last unit handed off; units run; unused
-// x2; HW_ID | XCC_ID << 32; unused x2.
+// Trace record of a (workgroup, phase), kTraceWords words written by the
+// control wave: real-time counter at the first unit of the phase, input
+// ready, input staged, first unit computed, first unit handed off, last unit
+// handed off; units run; first unit combined, its outputs written;
+// HW_ID | XCC_ID << 32; its partial sums landed, its outputs landed;
+// staging transfers issued, landed; two unused words.
 __device__ __forceinline__ unsigned long long now() { return __builtin_amdgcn_s_memrealtime(); }
 
 // ============================================================ compute waves
