@@ -27,7 +27,9 @@
 //    an item's dot products are done, across unit and phase boundaries, so
 //    a compute wave never waits for a store or a hand-off and its loads keep
 //    streaming while the control wave synchronises.  At the end of a unit
-//    the wave writes its per-row partial sums to LDS.
+//    the wave writes its per-row partial sums to LDS.  The two compute
+//    waves of a SIMD (w and w + 4) raise their priority on alternate items
+//    of a unit, the younger first, so they finish a unit together.
 //  * The control wave never loads weights.  It waits for the phase that
 //    writes a unit's input, stages the input chunk into LDS with
 //    load-to-LDS transfers, forms the input's RMS factors, adds the compute
@@ -849,6 +851,7 @@ struct CompState {
     int stb, stc;     // staged sub-blocks [stb, stb + stc) (as the control wave published them)
     ActLds A;
     float acc[2][M];  // the matrix being computed (gate, then up, of a fused pair)
+    uint32_t lead;    // 1 in the younger wave of a SIMD: it leads a unit's even items
 };
 
 // One ring step: consume the item in slot s (if the compute cursor is
@@ -872,7 +875,15 @@ __device__ __forceinline__ void ring_step(const Tab &tab, int n_phases, uint32_t
             st.A = act_lds<M>(act_base<M>(smem), st.stc, st.stb);
         }
     }
-    if (st.go) consume<M>(s, st.C, st.A, st.acc);
+    if (st.go) {
+        // The two compute waves of a SIMD take the lead in turns, one item
+        // each, the younger first.  At equal priority issue goes to the
+        // older wave, which then runs ahead and leaves the younger one to
+        // finish the unit alone, its latencies uncovered.
+        if ((static_cast<uint32_t>(st.C.item) + st.lead) & 1u) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+        consume<M>(s, st.C, st.A, st.acc);
+    }
     load_item(s, st.L);
     if (st.lv) st.lv = cur_advance_keep(tab, n_phases, b, G, st.L, wave, true);
     // a fused pair's gate sums are written after its last gate item
@@ -899,6 +910,7 @@ __device__ __forceinline__ void compute_waves(const Tab &tab, int n_phases, uint
     constexpr int D = RingDepth<M>::value;
     const int wave = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
     CompState<M> st;
+    st.lead = wave >= kCompWaves / 2 ? 1u : 0u;   // waves w and w + 4 share a SIMD
     st.lv = cur_init(tab, n_phases, b, G, st.L, wave, true);
     st.go = cur_init(tab, n_phases, b, G, st.C, wave, false);
     if (!st.go) return;
