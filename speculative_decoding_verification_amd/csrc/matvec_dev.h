@@ -1417,24 +1417,58 @@ __device__ __forceinline__ void finish_complete(const FinishIn &P, const UnitPos
             for (int mt = 0; mt < 3; mt++) {
                 if (mt < n_w) {
                     TileVals<M> f;
+                    // The partials of several position pairs are requested
+                    // before any is used: one memory round trip for up to three
+                    // pairs (M <= 6), one per two pairs up to M = 12 (more
+                    // registers held here spill), one per pair above.  A row
+                    // past N or a position past M reads an address that exists
+                    // (row N - 1, position M - 1, chunk 0) and is dropped.
+                    constexpr int KP = (M + 1) / 2, KG = KP <= 3 ? KP : 2;
+                    if constexpr (M <= 12) {
+                        const int64_t rc = min(row0 + r, N - 1);
 #pragma unroll
-                    for (int k = 0; k < (M + 1) / 2; k++) {
-                        const int m = h + 2 * k;
-                        float s = 0.0f;
-                        if (m < M && row0 + r < N) {
-                            const float *srcp = partial + (static_cast<int64_t>(mt) * SP * M + m) * N + row0 + r;
-                            float v[kMaxS];
+                        for (int k0 = 0; k0 < KP; k0 += KG) {
+                            float v[KG][kMaxS];
 #pragma unroll
-                            for (int c = 0; c < kMaxS; c++) {
-                                // every chunk's partial is requested before any is used
-                                const float xx = ld_dev(srcp + static_cast<int64_t>(c < S ? c : 0) * M * N);
-                                v[c] = c < S ? xx : 0.0f;
+                            for (int kk = 0; kk < KG; kk++) {
+                                const int mc = min(h + 2 * (k0 + kk), M - 1);
+                                const float *srcp = partial + (static_cast<int64_t>(mt) * SP * M + mc) * N + rc;
+#pragma unroll
+                                for (int c = 0; c < kMaxS; c++)
+                                    v[kk][c] = ld_dev(srcp + static_cast<int64_t>(c < S ? c : 0) * M * N);
                             }
 #pragma unroll
-                            for (int c = 0; c < kMaxS; c++)
-                                if (c < S) s += v[c];
+                            for (int kk = 0; kk < KG && k0 + kk < KP; kk++) {
+                                const int m = h + 2 * (k0 + kk);
+                                float s = 0.0f;
+                                if (m < M && row0 + r < N) {
+#pragma unroll
+                                    for (int c = 0; c < kMaxS; c++)
+                                        if (c < S) s += v[kk][c];
+                                }
+                                f.v[k0 + kk] = s * sh.rscale[min(m, M - 1)];
+                            }
                         }
-                        f.v[k] = s * sh.rscale[min(m, M - 1)];
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < KP; k++) {
+                            const int m = h + 2 * k;
+                            float s = 0.0f;
+                            if (m < M && row0 + r < N) {
+                                const float *srcp = partial + (static_cast<int64_t>(mt) * SP * M + m) * N + row0 + r;
+                                float v[kMaxS];
+#pragma unroll
+                                for (int c = 0; c < kMaxS; c++) {
+                                    // every chunk's partial is requested before any is used
+                                    const float xx = ld_dev(srcp + static_cast<int64_t>(c < S ? c : 0) * M * N);
+                                    v[c] = c < S ? xx : 0.0f;
+                                }
+#pragma unroll
+                                for (int c = 0; c < kMaxS; c++)
+                                    if (c < S) s += v[c];
+                            }
+                            f.v[k] = s * sh.rscale[min(m, M - 1)];
+                        }
                     }
                     store_y<M>(P, mt, row0, f);
                     if (mt == 0) {
