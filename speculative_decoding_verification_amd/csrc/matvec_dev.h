@@ -1225,15 +1225,25 @@ __device__ __forceinline__ void finish_tile(const PD &P, int64_t row0, const Til
     const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
     const int64_t N = P.N;
     const int rows_here = static_cast<int>(min(static_cast<int64_t>(kRows), N - row0));
+    // The lane reductions that end in a cross-half permute through LDS are
+    // formed for every position pair before any result is stored, so the
+    // pairs' round trips overlap instead of running one after another
+    // between the stores' branches.  Each pair's arithmetic is the same as
+    // alone.
+    constexpr int KP = (M + 1) / 2;
     unsigned long long *am = P.argmax;
     if (am) {
+        unsigned long long bk[KP];
 #pragma unroll
-        for (int k = 0; k < (M + 1) / 2; k++) {
-            const int m = h + 2 * k;
+        for (int k = 0; k < KP; k++) {
             const unsigned long long key =
                 r < rows_here ? pack_argmax(x.v[k], static_cast<uint32_t>(row0 + r)) : 0ull;
-            const unsigned long long bk = half_max64(key);
-            if (m < M && r == 0 && bk > sh.best[m]) sh.best[m] = bk;
+            bk[k] = half_max64(key);
+        }
+#pragma unroll
+        for (int k = 0; k < KP; k++) {
+            const int m = h + 2 * k;
+            if (m < M && r == 0 && bk[k] > sh.best[m]) sh.best[m] = bk[k];
         }
     }
     if (do_ep && P.ep_mode != SV_EP_NONE && rows_here == kRows) {
@@ -1242,25 +1252,29 @@ __device__ __forceinline__ void finish_tile(const PD &P, int64_t row0, const Til
         float *od = P.od, *osumsq = P.osumsq;
         int32_t *os16 = P.os16;
         const int64_t gb = row0 >> 5;
+        float vg[KP], amx[KP], sq[KP];
 #pragma unroll
-        for (int k = 0; k < (M + 1) / 2; k++) {
-            const int m = h + 2 * k;
+        for (int k = 0; k < KP; k++) {
             const float v = e.v[k];
-            const float vg = gamma ? v * g_row : v;
-            const float amx = half_max(fabsf(vg));
-            const float dd = amx / 127.0f;
+            vg[k] = gamma ? v * g_row : v;
+            amx[k] = half_max(fabsf(vg[k]));
+            sq[k] = half_sum(v * v);
+        }
+#pragma unroll
+        for (int k = 0; k < KP; k++) {
+            const int m = h + 2 * k;
+            const float dd = amx[k] / 127.0f;
             const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
-            float rq = roundf(vg * id);
+            float rq = roundf(vg[k] * id);
             rq = fminf(fmaxf(rq, -127.0f), 127.0f);
             const int qi = static_cast<int>(rq);
-            const int s = row_sum(qi);
-            const float sq = half_sum(v * v);
+            const int sm = row_sum(qi);
             if (m < M) {
                 st_dev(oq + m * N + row0 + r, static_cast<int8_t>(qi));
-                if ((r & 15) == 0) st_dev(os16 + m * (N >> 4) + 2 * gb + (r >> 4), s);
+                if ((r & 15) == 0) st_dev(os16 + m * (N >> 4) + 2 * gb + (r >> 4), sm);
                 if (r == 0) {
                     st_dev(od + m * (N >> 5) + gb, dd);
-                    st_dev(osumsq + m * (N >> 5) + gb, sq);
+                    st_dev(osumsq + m * (N >> 5) + gb, sq[k]);
                 }
             }
         }
