@@ -471,19 +471,32 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 // Reductions over the 32 lanes of a half-wave (every lane gets the result):
 // within each row of 16 by DPP, then the two rows by one lane exchange.
+// The two 16-lane rows of each half-wave side by side: v_permlane16_swap
+// with v in both operands leaves rows (0, 0, 2, 2) in the first result and
+// (1, 1, 3, 3) in the second, so a symmetric combine of the two gives each
+// lane the value of its row pair, with no LDS round trip.
+struct RowPair {
+    uint32_t a, b;
+};
+__device__ __forceinline__ RowPair row_pair(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return {static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])};
+}
 __device__ __forceinline__ float half_max(float v) {
     v = fmaxf(v, dpp_f<0xB1>(v));
     v = fmaxf(v, dpp_f<0x4E>(v));
     v = fmaxf(v, dpp_f<0x124>(v));
     v = fmaxf(v, dpp_f<0x128>(v));
-    return fmaxf(v, __shfl_xor(v, 16, 64));
+    const RowPair p = row_pair(__float_as_uint(v));
+    return fmaxf(__uint_as_float(p.a), __uint_as_float(p.b));
 }
 __device__ __forceinline__ float half_sum(float v) {
     v += dpp_f<0xB1>(v);
     v += dpp_f<0x4E>(v);
     v += dpp_f<0x124>(v);
     v += dpp_f<0x128>(v);
-    return v + __shfl_xor(v, 16, 64);
+    const RowPair p = row_pair(__float_as_uint(v));
+    return __uint_as_float(p.a) + __uint_as_float(p.b);
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
@@ -508,7 +521,10 @@ __device__ __forceinline__ unsigned long long half_max64(unsigned long long v) {
     v = umax64(v, dpp_u64<0x4E>(v));
     v = umax64(v, dpp_u64<0x124>(v));
     v = umax64(v, dpp_u64<0x128>(v));
-    return umax64(v, __shfl_xor(v, 16, 64));
+    const RowPair lo = row_pair(static_cast<uint32_t>(v & 0xFFFFFFFFull));
+    const RowPair hi = row_pair(static_cast<uint32_t>(v >> 32));
+    return umax64((static_cast<unsigned long long>(hi.a) << 32) | lo.a,
+                  (static_cast<unsigned long long>(hi.b) << 32) | lo.b);
 }
 
 // Workgroup barrier for LDS data only: waits for this wave's LDS
@@ -955,10 +971,14 @@ __device__ __forceinline__ bool wait_ready(const unsigned *ctr, unsigned target,
     for (;;) {
         __builtin_amdgcn_s_sleep(2);
         const unsigned bb = ld_dev(slot);
-        unsigned v = (lane < kSlots) ? a : 0u;
-#pragma unroll
-        for (int o = 4; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-        v = __shfl(v, 0, 64);
+        // the kSlots = 8 slots in lanes 0-7, added in lane 0 by data-parallel
+        // moves (no LDS round trip), then read as a scalar
+        static_assert(kSlots == 8, "the poll adds one group of eight lanes");
+        int t = (lane < kSlots) ? static_cast<int>(a) : 0;
+        t += dpp_i<0xB1>(t);    // quad_perm [1,0,3,2]
+        t += dpp_i<0x4E>(t);    // quad_perm [2,3,0,1]
+        t += dpp_i<0x104>(t);   // row_shl:4
+        const unsigned v = static_cast<unsigned>(__builtin_amdgcn_readlane(t, 0));
         if (v >= target) return true;
         if (++n > kSpinLimit || ((n & 63u) == 0u && ld_dev(status) != 0u)) {
             if (lane == 0) or_dev(status, 1u);
@@ -1423,7 +1443,7 @@ __device__ __forceinline__ void finish_complete(const FinishIn &P, const UnitPos
         unsigned *tc = P.tile_count;
         unsigned prev = 0;
         if (lane == 0) prev = add_dev(tc + g.tile, 1u);
-        prev = static_cast<unsigned>(__shfl(static_cast<int>(prev), 0, 64));
+        prev = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(prev), 0));
         if (prev == static_cast<unsigned>(S * P.mu - 1)) {
             const int n_w = P.n_w, src = P.ep_src;
             TileVals<M> f0, e;
