@@ -1138,8 +1138,6 @@ __device__ __forceinline__ void stage(const StageIn &P, const UnitPos &g, uint8_
     stage_field<M, 32>(act, reinterpret_cast<const uint8_t *>(P.aq) + static_cast<int64_t>(sb) * 32, K, cs);
     stage_field<M, 4>(act + M * rs * 32, reinterpret_cast<const uint8_t *>(P.ad + sb), nsub * 4, cs);
     stage_field<M, 8>(act + M * rs * 36, reinterpret_cast<const uint8_t *>(P.as16 + 2 * sb), (K >> 4) * 4, cs);
-    if (P.parts && P.parts_lds)
-        dma_copy(act + M * row_sub<M>(cs) * kActRec, reinterpret_cast<const uint8_t *>(P.parts), M * P.n_parts * 4);
     if (tr && lane == 0) tr[12] = now();
     // the transfers have written LDS once this wave's loads are complete
     __builtin_amdgcn_s_waitcnt(0);
@@ -1595,7 +1593,17 @@ __device__ __forceinline__ void control_wave(const Tab &tab, int n_phases, uint3
             }
             lds_barrier();   // B1
             if (sh.abort) break;
-            if (fresh) stage_rscale<M>(si, g, act, sh);
+            if (fresh) {
+                // the input's RMS partials feed only this wave's finish: they
+                // are staged after the compute waves are let go, so their
+                // transfers do not hold up the barrier
+                if (si.parts && si.parts_lds) {
+                    dma_copy(act + M * row_sub<M>(g.pcs) * kActRec, reinterpret_cast<const uint8_t *>(si.parts),
+                             M * si.n_parts * 4);
+                    __builtin_amdgcn_s_waitcnt(0);
+                }
+                stage_rscale<M>(si, g, act, sh);
+            }
         }
         const FinishIn fi = finish_in(P);       // in flight while the unit computes
         const float g_cur = gamma_of(fi, g);
