@@ -135,6 +135,22 @@ SHAPES = [(96, 1024), (64, 2560), (160, 5120), (32, 768), (64, 9728), (32, 17408
 @pytest.mark.parametrize("N,K", SHAPES)
 @pytest.mark.parametrize("M", [1, 2, 5, 8, 16])
 def test_matvec_parity(gu, orc, qt, N, K, M):
+    _check_matvec(gu, orc, qt, N, K, M)
+
+
+@pytest.mark.parametrize("qt", QT)
+@pytest.mark.parametrize("N,K", [(64, 9728), (32, 17408)])
+@pytest.mark.parametrize("M", [7, 10, 12, 13])
+def test_matvec_parity_split_combine(gu, orc, qt, N, K, M):
+    """Tiles split over K (two and four chunks) where the tile's last unit
+    reloads the partials in rounds of two position pairs (M = 7..12: at
+    M = 10 the last round holds one pair, at M = 7 the last pair has one
+    position past M, at M = 12 every round is full) or one pair at a time
+    (M = 13)."""
+    _check_matvec(gu, orc, qt, N, K, M)
+
+
+def _check_matvec(gu, orc, qt, N, K, M):
     import speculative_decoding_verification_amd as sv
     if qt != 8 and K % 256:
         pytest.skip("K-quants need K % 256 == 0")
