@@ -848,14 +848,22 @@ __device__ __forceinline__ void put_partials(float *wp, float (&acc)[2][M], int 
     const int lane = threadIdx.x & 63;
     const int wave = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
     const int grp = lane >> 3, jl = lane & 7;
+    // every sum first (independent chains that fill each other's data-
+    // parallel-move wait states), then the stores under one lane mask
 #pragma unroll
     for (int p = 0; p < 2; p++)
 #pragma unroll
-        for (int m = 0; m < M; m++) {
-            const float v = group8_sum(acc[p][m]);
-            if (jl == 0) wp[((wave * NMat<M>::value + mm) * M + m) * 16 + grp * 2 + p] = v;
-            acc[p][m] = 0.0f;
-        }
+        for (int m = 0; m < M; m++) acc[p][m] = group8_sum(acc[p][m]);
+    if (jl == 0) {
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+            for (int m = 0; m < M; m++) wp[((wave * NMat<M>::value + mm) * M + m) * 16 + grp * 2 + p] = acc[p][m];
+    }
+#pragma unroll
+    for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int m = 0; m < M; m++) acc[p][m] = 0.0f;
 }
 
 // State of a compute wave between ring items.
