@@ -1167,12 +1167,26 @@ __device__ __forceinline__ void stage_rscale(const StageIn &P, const UnitPos &g,
         return;
     }
     const float *lp = reinterpret_cast<const float *>(act + M * row_sub<M>(g.pcs) * kActRec);
+    if (P.parts_lds) {
+        // every position's partials of a lane at once (the positions'
+        // reads and lane sums overlap); each position's adds keep their order
+        float t[M];
+#pragma unroll
+        for (int m = 0; m < M; m++) t[m] = 0.0f;
+        for (int i = lane; i < n_parts; i += 64)
+#pragma unroll
+            for (int m = 0; m < M; m++) t[m] += lp[m * n_parts + i];
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float tot = wave_sum(t[m]);
+            if (lane == 0) sh.rscale[m] = 1.0f / sqrtf(tot / static_cast<float>(K) + P.eps);
+        }
+        return;
+    }
 #pragma unroll 1
     for (int m = 0; m < M; m++) {
         float t = 0.0f;
-        if (P.parts_lds) {
-            for (int i = lane; i < n_parts; i += 64) t += lp[m * n_parts + i];
-        } else {
+        {
             const float *gp = P.parts + m * n_parts;
             float v[kPartsPerLane];
 #pragma unroll
