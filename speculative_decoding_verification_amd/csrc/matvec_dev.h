@@ -28,8 +28,8 @@
 //    a compute wave never waits for a store or a hand-off and its loads keep
 //    streaming while the control wave synchronises.  At the end of a unit
 //    the wave writes its per-row partial sums to LDS.  The two compute
-//    waves of a SIMD (w and w + 4) raise their priority on alternate items
-//    of a unit, the younger first, so they finish a unit together.
+//    waves of a SIMD (w and w + 4) raise their priority in turns, two items
+//    of a unit each, the younger first, so they finish a unit together.
 //  * The control wave never loads weights.  It waits for the phase that
 //    writes a unit's input, stages the input chunk into LDS with
 //    load-to-LDS transfers, forms the input's RMS factors, adds the compute
@@ -875,7 +875,7 @@ struct CompState {
     int stb, stc;     // staged sub-blocks [stb, stb + stc) (as the control wave published them)
     ActLds A;
     float acc[2][M];  // the matrix being computed (gate, then up, of a fused pair)
-    uint32_t lead;    // 1 in the younger wave of a SIMD: it leads a unit's even items
+    uint32_t lead;    // 1 in the younger wave of a SIMD: it leads a unit's items 0-1, 4-5, ...
 };
 
 // One ring step: consume the item in slot s (if the compute cursor is
@@ -900,11 +900,11 @@ __device__ __forceinline__ void ring_step(const Tab &tab, int n_phases, uint32_t
         }
     }
     if (st.go) {
-        // The two compute waves of a SIMD take the lead in turns, one item
+        // The two compute waves of a SIMD take the lead in turns, two items
         // each, the younger first.  At equal priority issue goes to the
         // older wave, which then runs ahead and leaves the younger one to
         // finish the unit alone, its latencies uncovered.
-        if ((static_cast<uint32_t>(st.C.item) + st.lead) & 1u) __builtin_amdgcn_s_setprio(1);
+        if (((static_cast<uint32_t>(st.C.item) >> 1) + st.lead) & 1u) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
         consume<M>(s, st.C, st.A, st.acc);
     }
